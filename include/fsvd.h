@@ -1,0 +1,248 @@
+/*
+ * fsvd.h - C ABI of the fused low-rank transformer-layer library for AMD Instinct MI355X (gfx950).
+ *
+ * The library implements the serving hot path of an SVD-compressed transformer layer: every
+ * dense projection W is replaced by a factor pair and applied as y = (x . U) . V, with the
+ * rank-r intermediate kept in on-chip tiles, on packed Q/K/V and O projections and on a packed
+ * gate|up SwiGLU MLP (GELU for encoder layers), feeding attention over a contiguous dense KV
+ * cache; each layer's decode step can be captured once as a hipGraph and replayed per token.
+ *
+ * Sources, cited by page title and section:
+ *   [V1]    "FlashSVD: Memory-Efficient Inference with Streaming for Low-Rank Models", abstract:
+ *           fused low-rank projections in attention and FFN; factor tiles streamed through
+ *           on-chip memory so full-size activation buffers are never materialised.
+ *   [V15-M1] "FlashSVD v1.5: Making Low-Rank Transformers Inference Actually Fast" (explainer),
+ *           Methodology 1, Unified Runtime Abstraction: one common factorized representation.
+ *   [V15-M2] same page, Methodology 2, Dense-KV Attention: rebuild dense Q/K/V for the current
+ *           tokens only, keep history in a contiguous dense KV cache read in one attention step.
+ *   [V15-M3] same page, Methodology 3, Packed MLP Execution: gate and up input-side factors
+ *           packed offline into one tensor, one wide projection, then a split.
+ *   [V15-M4] same page, Methodology 4, Per-Layer CUDA Graph Replay: the stable small-batch decode
+ *           body of each layer captured once and replayed.
+ *
+ * General conventions (apply to every call unless its comment says otherwise)
+ *   - Pointers are DEVICE pointers unless marked (host).  Matrices are row-major; "ld" is the row
+ *     stride in elements.  Activations are row vectors: y = x . U . V.
+ *   - Factor storage ("common factorized representation"): a projection of input width K and
+ *     output width N with rank r is stored as Ut = U^T [r, K] (row i = input-side factor of rank
+ *     component i) and Vt = V^T [N, r], both K-contiguous like two linear-layer weights.
+ *   - Ranks passed to the library are STORED ranks: they must be multiples of 8 (bf16) or 4
+ *     (fp32) so rows are 16-byte vectors.  A caller whose logical rank is not a multiple pads
+ *     Ut with zero rows and Vt with zero columns (fsvd_prepack does this); padding is exact.
+ *   - Alignment: every pointer must be 16-byte aligned and every ld * element size a multiple
+ *     of 16 bytes.  Hidden sizes K, N must be multiples of 8 (bf16) / 4 (fp32).
+ *   - dtype: FSVD_BF16 means bf16 storage for every tensor of the call (weights, activations,
+ *     outputs, KV cache), fp32 accumulation, fp32 softmax; FSVD_F32 means fp32 throughout.
+ *     Documented bf16 rounding points: the normalised input of a projection, the rank
+ *     activations z, and the MLP product t are rounded to bf16 before their next product.
+ *   - Ownership: the caller owns every buffer, including the workspace ("ws").  The library
+ *     never allocates device memory inside these calls and never synchronises, except where a
+ *     call says so (capture, poll).
+ *   - Workspace: each call that needs scratch takes (ws, ws_bytes); the matching *_ws() query
+ *     returns the size.  The first 256 bytes of every workspace are a header whose first int32
+ *     is the DEVICE ERROR WORD; a workspace must be zero-filled once before its first use.
+ *   - Errors: every call returns fsvd_status_t.  Arguments are validated before any launch
+ *     (null pointers, non-positive sizes, misalignment, too-small workspace, unsupported
+ *     combinations); on failure nothing is launched and fsvd_last_error() explains.  Launch
+ *     failures return FSVD_ERR_HIP.  Conditions only the device can see (a KV position at or
+ *     beyond L_max) skip the offending write, never write out of bounds, and set the device
+ *     error word, which fsvd_poll_device_error() reads.  C++ exceptions never cross the ABI.
+ *   - Streams: every call is asynchronous on the caller's hipStream_t (0 = default stream).
+ *   - Thread safety: calls are stateless apart from graph objects and the thread-local error
+ *     string; concurrent calls on different streams must use different workspaces.
+ */
+#ifndef FSVD_H
+#define FSVD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* fsvd_stream_t; /* a hipStream_t */
+
+#define FSVD_ABI_VERSION 1
+
+typedef enum {
+    FSVD_OK = 0,
+    FSVD_ERR_INVALID_ARG = 1, /* bad pointer, size, alignment or leading dimension */
+    FSVD_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. dtype for this call) */
+    FSVD_ERR_WORKSPACE = 3,   /* ws_bytes smaller than the *_ws() query */
+    FSVD_ERR_HIP = 4,         /* a HIP runtime call failed (launch, capture, copy) */
+    FSVD_ERR_CAPTURE = 5,     /* graph capture / instantiate / replay failed or graph destroyed */
+    FSVD_ERR_DEVICE = 6       /* poll found a non-zero device error word */
+} fsvd_status_t;
+
+typedef enum { FSVD_F32 = 0, FSVD_BF16 = 1 } fsvd_dtype_t;
+typedef enum { FSVD_ACT_SWIGLU = 0, FSVD_ACT_GELU = 1 } fsvd_act_t;
+
+/* Device error word bits (OR-ed). */
+#define FSVD_DEVERR_KV_OVERFLOW 0x1 /* a token position >= L_max: its KV write was skipped */
+#define FSVD_DEVERR_SEQ_OVERFLOW 0x2 /* attention length > L_max: clamped to L_max */
+
+int fsvd_abi_version(void);
+const char* fsvd_status_str(fsvd_status_t s); /* static string */
+const char* fsvd_last_error(void);            /* thread-local detail of this thread's last failure */
+
+/* ------------------------------------------------------------------------------------------
+ * a1. Offline prepack  [V15-M3] (input-side factors that share an input are packed into one
+ * tensor; this library also packs Q/K/V that way).  Not on the timed path.
+ *
+ * Writes the n_items source matrices one below the other into dst [sum(rows_pad), cols_pad]
+ * (row stride ld_dst >= cols_pad): item i occupies rows_pad[i] rows; its first rows[i] rows
+ * hold src[i] (columns [0, cols[i]), the rest of the row zero) and the remaining rows are
+ * zero.  Used both to stack Ut blocks (A_qkv = [Ut_q; Ut_k; Ut_v], A_gu = [Ut_gate; Ut_up],
+ * each rank padded to a multiple of 8) and to zero-pad the rank columns of a Vt.
+ * Bit-exact copy.  items is a HOST array; src pointers are device pointers.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct {
+    const void* src;
+    int64_t rows, cols, ld_src; /* source extent and row stride (elements) */
+    int64_t rows_pad;           /* rows this item occupies in dst (>= rows) */
+} fsvd_pack_item;
+
+fsvd_status_t fsvd_prepack(void* dst, int64_t ld_dst, int64_t cols_pad, const fsvd_pack_item* items /*host*/,
+                           int n_items, fsvd_dtype_t dtype, fsvd_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * a2+a3. Fused low-rank linear  [V1] [V15-M1]
+ *   y[m, :] = residual[m, :] + bias + (x[m, :] . Ut^T) . Vt^T        (z = x . Ut^T is rank-r)
+ * x [M, K] (ldx), Ut [r, K] (ldu), Vt [N, r] (ldv), bias [N] or NULL, residual [M, N] (ldr)
+ * or NULL (may alias y for in-place accumulation), y [M, N] (ldy).  dtype FSVD_F32 or FSVD_BF16.
+ * Decode-sized M (<= 32) runs the HBM-streaming row-dot kernels (z passes through the
+ * workspace as a B x r vector); larger M runs the bf16 MFMA path (bf16 only).
+ * ------------------------------------------------------------------------------------------ */
+size_t fsvd_lowrank_linear_ws(int64_t M, int64_t K, int64_t r, int64_t N, fsvd_dtype_t dtype);
+fsvd_status_t fsvd_lowrank_linear(const void* x, int64_t M, int64_t K, int64_t ldx,
+                                  const void* Ut, int64_t r, int64_t ldu,
+                                  const void* Vt, int64_t N, int64_t ldv,
+                                  const void* bias, const void* residual, int64_t ldr,
+                                  void* y, int64_t ldy, fsvd_dtype_t dtype,
+                                  void* ws, size_t ws_bytes, fsvd_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * a2+a3+a5. Packed Q/K/V projection with KV append  [V15-M2] [V15-M3]
+ *   a = RMSNorm(x) (if norm_w) = x / sqrt(mean(x^2) + eps) * norm_w, else x
+ *   [z_q | z_k | z_v] = a . A_qkv^T   (one wide projection, split at r_q and r_q + r_k)
+ *   q = z_q . Vt_q^T, k = z_k . Vt_k^T, v = z_v . Vt_v^T; RoPE (rotate-half, pair (i, i+D/2)
+ *   turned by angle p * theta^(-2i/D)) on q and k when rope_theta > 0, at position
+ *   p = cache_seqlens[b] + s for token s of sequence b;
+ *   q -> q_out [B, S, Hq, D]; k, v -> k_cache, v_cache [B, L_max, Hkv, D] at position p
+ *   (bit-exact copy of the bf16 k/v); optional k_out, v_out [B, S, Hkv, D] (NULL = skip)
+ *   receive the same bits (for checking).
+ * x [B, S, d] contiguous; A_qkv [r_q + r_k + r_v, d]; Vt_q [Hq*D, r_q], Vt_k [Hkv*D, r_k],
+ * Vt_v [Hkv*D, r_v] contiguous; cache_seqlens [B] int32 = tokens already cached (read only).
+ * Positions >= L_max: the KV write is skipped and FSVD_DEVERR_KV_OVERFLOW set.  bf16 only.
+ * ------------------------------------------------------------------------------------------ */
+size_t fsvd_lowrank_qkv_ws(int64_t B, int64_t S, int64_t d, int64_t r_q, int64_t r_k, int64_t r_v,
+                           int64_t Hq, int64_t Hkv, int64_t D);
+fsvd_status_t fsvd_lowrank_qkv(const void* x, int64_t B, int64_t S, int64_t d,
+                               const void* norm_w, float norm_eps,
+                               const void* A_qkv, int64_t r_q, int64_t r_k, int64_t r_v,
+                               const void* Vt_q, const void* Vt_k, const void* Vt_v,
+                               int64_t Hq, int64_t Hkv, int64_t D, float rope_theta,
+                               void* q_out, void* k_cache, void* v_cache, int64_t L_max,
+                               const int32_t* cache_seqlens, void* k_out, void* v_out,
+                               fsvd_dtype_t dtype, void* ws, size_t ws_bytes, fsvd_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * a2+a3+a4. Packed low-rank MLP  [V15-M3] [V1]
+ *   b = RMSNorm(x) if norm_w else x
+ *   z = b . A_gu^T, z_g = z[:, :r_g], z_u = z[:, r_g:r_g+r_u]   (A_gu = [Ut_gate; Ut_up])
+ *   SWIGLU: t = SiLU(z_g . Vt_g^T) * (z_u . Vt_u^T);  GELU: t = GELU(z_u . Vt_u^T) (r_g = 0,
+ *   Vt_g NULL; exact erf form);  y = residual + (t . Ut_d^T) . Vt_d^T
+ * x [M, d]; A_gu [r_g + r_u, d]; Vt_g, Vt_u [d_ff, r_g|r_u]; Ut_d [r_d, d_ff]; Vt_d [d, r_d];
+ * residual [M, d] or NULL (may alias y); y [M, d].  All contiguous.  bf16 only.
+ * The d_ff-wide g, u, t never reach HBM on the MFMA path; at decode sizes t passes through
+ * the workspace as a B x d_ff vector.
+ * ------------------------------------------------------------------------------------------ */
+size_t fsvd_lowrank_mlp_packed_ws(int64_t M, int64_t d, int64_t r_g, int64_t r_u, int64_t d_ff, int64_t r_d);
+fsvd_status_t fsvd_lowrank_mlp_packed(const void* x, int64_t M, int64_t d,
+                                      const void* norm_w, float norm_eps, fsvd_act_t act,
+                                      const void* A_gu, int64_t r_g, int64_t r_u,
+                                      const void* Vt_g, const void* Vt_u, int64_t d_ff,
+                                      const void* Ut_d, const void* Vt_d, int64_t r_d,
+                                      const void* residual, void* y, fsvd_dtype_t dtype,
+                                      void* ws, size_t ws_bytes, fsvd_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * a6. Attention over the contiguous dense KV cache  [V15-M2]
+ *   o[b, s, h] = sum_{j < n} softmax_j(scale * q[b, s, h] . k[b, j, g]) v[b, j, g],
+ *   g = floor(h * Hkv / Hq), n = cache_seqlens[b] + s + 1 (causal) or cache_seqlens[b] + Sq.
+ * q, out [B, Sq, Hq, D]; caches [B, L_max, Hkv, D]; cache_seqlens [B] int32 = valid length
+ * BEFORE this call's Sq tokens were appended (they must already be in the cache).
+ * softmax_scale 0 -> 1/sqrt(D).  Sq == 1 uses split-length partitions merged by log-sum-exp
+ * (the partition count is fixed by the workspace; lengths are read on the device, so a
+ * captured graph stays valid as the cache grows).  Sq > 1 is the correctness path used by
+ * prefill and encoder layers.  D must be 64 or 128; Hq % Hkv == 0.  bf16 only.
+ * n > L_max is clamped to L_max and sets FSVD_DEVERR_SEQ_OVERFLOW.
+ * ------------------------------------------------------------------------------------------ */
+size_t fsvd_decode_attn_dense_kv_ws(int64_t B, int64_t Sq, int64_t Hq, int64_t Hkv, int64_t D, int64_t L_max);
+fsvd_status_t fsvd_decode_attn_dense_kv(const void* q, const void* k_cache, const void* v_cache, int64_t L_max,
+                                        const int32_t* cache_seqlens, int64_t B, int64_t Sq, int64_t Hq,
+                                        int64_t Hkv, int64_t D, float softmax_scale, int causal, void* out,
+                                        fsvd_dtype_t dtype, void* ws, size_t ws_bytes, fsvd_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * a7. Layer glue: y = LayerNorm(x + residual) * gamma + beta over rows of width d (BERT
+ * post-norm); residual may be NULL; y may alias x.  bf16 only.  Llama-style RMSNorm is fused
+ * into fsvd_lowrank_qkv / fsvd_lowrank_mlp_packed, residual adds into their epilogues.
+ * ------------------------------------------------------------------------------------------ */
+fsvd_status_t fsvd_layernorm(const void* x, const void* residual, const void* gamma, const void* beta,
+                             float eps, int64_t M, int64_t d, void* y, fsvd_dtype_t dtype, fsvd_stream_t stream);
+
+/* cache_seqlens[b] += n for b < B (one tiny kernel; also the optional last node of a graph). */
+fsvd_status_t fsvd_seqlens_advance(int32_t* cache_seqlens, int64_t B, int32_t n, fsvd_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * a7+a8. Whole Llama-style pre-norm decoder layer and its per-layer graph  [V15-M4]
+ *   a = RMSNorm(x); q,k,v (RoPE, append) ; o = attention ; h = x + O(o) ;
+ *   y = h + MLP(RMSNorm(h))
+ * over S new tokens per sequence (S == 1 is a decode step; S > 1 a causal prefill that
+ * appends at cache_seqlens[b]).  Every pointer in the descriptor is a device pointer that the
+ * caller keeps alive (and, for a captured graph, at a fixed address) until the last use.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct fsvd_decoder_layer_desc {
+    int64_t B, S, d, Hq, Hkv, D, d_ff, L_max;
+    int64_t r_q, r_k, r_v, r_o, r_g, r_u, r_d; /* stored (padded) ranks */
+    float norm_eps, rope_theta, softmax_scale;  /* rope_theta 0 -> no RoPE; scale 0 -> 1/sqrt(D) */
+    int32_t advance_seqlens;                    /* 1: cache_seqlens += S after the layer */
+    int32_t reserved;
+    const void* x; /* [B, S, d] layer input */
+    void* y;       /* [B, S, d] layer output (must not alias x) */
+    const void* attn_norm_w;                    /* [d] */
+    const void* mlp_norm_w;                     /* [d] */
+    const void* A_qkv;                          /* [r_q + r_k + r_v, d] */
+    const void *Vt_q, *Vt_k, *Vt_v;             /* [Hq*D, r_q], [Hkv*D, r_k], [Hkv*D, r_v] */
+    const void *Ut_o, *Vt_o;                    /* [r_o, Hq*D], [d, r_o] */
+    const void* A_gu;                           /* [r_g + r_u, d] */
+    const void *Vt_g, *Vt_u;                    /* [d_ff, r_g], [d_ff, r_u] */
+    const void *Ut_d, *Vt_d;                    /* [r_d, d_ff], [d, r_d] */
+    void *k_cache, *v_cache;                    /* [B, L_max, Hkv, D] */
+    int32_t* cache_seqlens;                     /* [B] */
+    void* ws;
+    size_t ws_bytes;
+} fsvd_decoder_layer_desc;
+
+typedef struct fsvd_graph fsvd_graph; /* opaque */
+
+size_t fsvd_decoder_layer_ws(const fsvd_decoder_layer_desc* desc /*host*/);
+/* Eager: launches the layer's kernels on stream (same kernels the graph holds). bf16 only. */
+fsvd_status_t fsvd_decoder_layer_run(const fsvd_decoder_layer_desc* desc /*host*/, fsvd_stream_t stream);
+/* Captures the layer (S must be 1) into a hipGraph on a library-owned capture stream and
+ * instantiates it; synchronises the device once.  *out receives the graph handle (host). */
+fsvd_status_t fsvd_decoder_layer_capture(const fsvd_decoder_layer_desc* desc /*host*/, fsvd_graph** out);
+/* One hipGraphLaunch of the captured layer on stream. */
+fsvd_status_t fsvd_graph_replay(fsvd_graph* g, fsvd_stream_t stream);
+fsvd_status_t fsvd_graph_destroy(fsvd_graph* g);
+
+/* Reads (synchronising stream) and clears the device error word of a workspace; *code (host)
+ * receives its value; returns FSVD_ERR_DEVICE when it was non-zero. */
+fsvd_status_t fsvd_poll_device_error(void* ws, fsvd_stream_t stream, int32_t* code /*host*/);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FSVD_H */

@@ -1,0 +1,109 @@
+// Shared device helpers and host-side status plumbing for the fsvd library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include <algorithm>
+
+#include "../../include/fsvd.h"
+
+namespace fsvd {
+
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ bf16 <-> fp32
+
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+// round-to-nearest-even fp32 -> bf16 (hardware conversion on gfx950)
+__device__ __forceinline__ bf16_t f2bf(float f) {
+    __bf16 h = static_cast<__bf16>(f);
+    return __builtin_bit_cast(bf16_t, h);
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// a.x*b.x + a.y*b.y + c on two packed bf16 pairs, fp32 accumulate
+__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a), __builtin_bit_cast(bf16x2_v, b), c,
+                                           false);
+}
+
+// ------------------------------------------------------------------ cross-lane reductions (DPP)
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// every lane of each 16-lane row receives the sum over its row
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f<0x124>(v);  // row_ror:4
+    v += dpp_f<0x128>(v);  // row_ror:8
+    return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x124>(v));
+    v = fmaxf(v, dpp_f<0x128>(v));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0)) +
+           __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16)) +
+           __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32)) +
+           __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+}
+
+// ------------------------------------------------------------------ activations
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+__device__ __forceinline__ float gelu_f(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); }
+
+// RoPE angle for pair i of a head of width D at position p: p * theta^(-2i/D), reduced mod 2*pi in
+// double so long positions keep fp32 accuracy in sin/cos.
+__device__ __forceinline__ void rope_cs(int64_t p, int i, int D, float theta, float* c, float* s) {
+    double inv = exp2(-2.0 * (double)i / (double)D * log2((double)theta));
+    double ang = (double)p * inv;
+    const double two_pi = 6.283185307179586476925286766559;
+    ang = ang - two_pi * floor(ang / two_pi);
+    sincosf((float)ang, s, c);
+}
+
+// device error word: first int32 of every workspace header
+__device__ __forceinline__ void set_dev_error(int* err, int bits) {
+    if (err) atomicOr(err, bits);
+}
+
+}  // namespace fsvd
+
+// ------------------------------------------------------------------ host-side plumbing
+
+namespace fsvd {
+constexpr size_t kWsHeader = 256;
+
+void set_error(const char* fmt, ...);
+fsvd_status_t fail(fsvd_status_t s, const char* fmt, ...);
+
+inline bool aligned16(const void* p) { return (((uintptr_t)p) & 15u) == 0; }
+inline size_t esize(fsvd_dtype_t t) { return t == FSVD_F32 ? 4 : 2; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// status of the last kernel launch
+fsvd_status_t check_launch(const char* what);
+}  // namespace fsvd
+
+#define FSVD_REQUIRE(cond, ...)                                  \
+    do {                                                         \
+        if (!(cond)) return ::fsvd::fail(FSVD_ERR_INVALID_ARG, __VA_ARGS__); \
+    } while (0)

@@ -1,0 +1,111 @@
+// Small kernels around the projections: the offline factor prepack, BERT-style post-norm
+// LayerNorm, the cache-length advance, and the RMSNorm preparation of the MFMA (prefill) path.
+#include "kernels.h"
+
+namespace fsvd {
+
+namespace {
+
+// prepack: copy one item (rows x cols, 16-bit or 32-bit elements) into dst rows
+// [row0, row0 + rows_pad) x [0, cols_pad), zero-filling the pad area.  One thread per element.
+template <typename E>
+__global__ void prepack_kernel(E* dst, int64_t ld_dst, int64_t cols_pad, int64_t row0, const E* src, int64_t rows,
+                               int64_t cols, int64_t ld_src, int64_t rows_pad) {
+    const int64_t total = rows_pad * cols_pad;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / cols_pad, c = i - r * cols_pad;
+        dst[(row0 + r) * ld_dst + c] = (r < rows && c < cols) ? src[r * ld_src + c] : E(0);
+    }
+}
+
+// y = LayerNorm(x + res) * g + b over rows of width d; one workgroup per row, fp32 statistics
+__global__ __launch_bounds__(256) void layernorm_kernel(const bf16_t* x, const bf16_t* res, const bf16_t* g,
+                                                        const bf16_t* bta, float eps, int64_t d, bf16_t* y) {
+    const int64_t row = blockIdx.x;
+    const bf16_t* xr = x + row * d;
+    const bf16_t* rr = res ? res + row * d : nullptr;
+    extern __shared__ float buf[];  // d floats
+    __shared__ float red[8];
+    float s = 0.f;
+    for (int64_t i = threadIdx.x; i < d; i += 256) {
+        const float v = bf2f(xr[i]) + (rr ? bf2f(rr[i]) : 0.f);
+        buf[i] = v;
+        s += v;
+    }
+    s = wave_sum(s);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = s;
+    __syncthreads();
+    const float mean = (red[0] + red[1] + red[2] + red[3]) / (float)d;
+    float q = 0.f;
+    for (int64_t i = threadIdx.x; i < d; i += 256) {
+        const float dv = buf[i] - mean;
+        q += dv * dv;
+    }
+    q = wave_sum(q);
+    if ((threadIdx.x & 63) == 0) red[4 + w] = q;
+    __syncthreads();
+    const float rstd = 1.0f / sqrtf((red[4] + red[5] + red[6] + red[7]) / (float)d + eps);
+    for (int64_t i = threadIdx.x; i < d; i += 256)
+        y[row * d + i] = f2bf((buf[i] - mean) * rstd * bf2f(g[i]) + bf2f(bta[i]));
+}
+
+__global__ void seqlens_advance_kernel(int32_t* sl, int64_t B, int32_t n) {
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i < B) sl[i] += n;
+}
+
+// rstd[m] = 1/sqrt(mean(x^2) + eps); xn[m, :] = bf16(x * w) (w may be null = ones)
+__global__ __launch_bounds__(256) void rms_prep_kernel(const bf16_t* x, const bf16_t* w, float eps, int64_t d,
+                                                       bf16_t* xn, float* rstd) {
+    const int64_t row = blockIdx.x;
+    const bf16_t* xr = x + row * d;
+    __shared__ float red[4];
+    float s = 0.f;
+    for (int64_t i = threadIdx.x; i < d; i += 256) {
+        const float v = bf2f(xr[i]);
+        s += v * v;
+        xn[row * d + i] = w ? f2bf(v * bf2f(w[i])) : xr[i];
+    }
+    s = wave_sum(s);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) rstd[row] = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
+}
+
+}  // namespace
+
+fsvd_status_t launch_prepack(void* dst, int64_t ld_dst, int64_t cols_pad, int64_t row0, const void* src, int64_t rows,
+                             int64_t cols, int64_t ld_src, int64_t rows_pad, size_t es, hipStream_t st) {
+    const int64_t total = rows_pad * cols_pad;
+    if (total == 0) return FSVD_OK;
+    const int grid = (int)std::min<int64_t>((total + 255) / 256, 65536);
+    if (es == 2)
+        prepack_kernel<uint16_t><<<grid, 256, 0, st>>>((uint16_t*)dst, ld_dst, cols_pad, row0, (const uint16_t*)src,
+                                                        rows, cols, ld_src, rows_pad);
+    else
+        prepack_kernel<uint32_t><<<grid, 256, 0, st>>>((uint32_t*)dst, ld_dst, cols_pad, row0, (const uint32_t*)src,
+                                                        rows, cols, ld_src, rows_pad);
+    return check_launch("prepack");
+}
+
+fsvd_status_t launch_layernorm(const bf16_t* x, const bf16_t* res, const bf16_t* g, const bf16_t* b, float eps,
+                               int64_t M, int64_t d, bf16_t* y, hipStream_t st) {
+    if (M == 0) return FSVD_OK;
+    layernorm_kernel<<<(unsigned)M, 256, d * sizeof(float), st>>>(x, res, g, b, eps, d, y);
+    return check_launch("layernorm");
+}
+
+fsvd_status_t launch_seqlens_advance(int32_t* sl, int64_t B, int32_t n, hipStream_t st) {
+    seqlens_advance_kernel<<<(unsigned)((B + 63) / 64), 64, 0, st>>>(sl, B, n);
+    return check_launch("seqlens_advance");
+}
+
+fsvd_status_t launch_rms_prep(const bf16_t* x, const bf16_t* w, float eps, int64_t M, int64_t d, bf16_t* xn,
+                              float* rstd, hipStream_t st) {
+    if (M == 0) return FSVD_OK;
+    rms_prep_kernel<<<(unsigned)M, 256, 0, st>>>(x, w, eps, d, xn, rstd);
+    return check_launch("rms_prep");
+}
+
+}  // namespace fsvd

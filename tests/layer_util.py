@@ -1,0 +1,96 @@
+"""Device-side helpers for the GPU tests, the smoke check and the benchmark: upload host arrays,
+prepack factors through the library's own fsvd_prepack, and hold one decoder layer's buffers and
+descriptor.  No arithmetic of the method lives here (and nothing here imports the oracle)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from svd_compressed_transformer_amd import fsvd
+from svd_compressed_transformer_amd.inputs import round_up
+
+PAD = 8  # stored ranks are padded to a multiple of 8 (16-byte bf16 rows)
+
+
+def to_dev(a, dtype=torch.bfloat16, device="cuda"):
+    """Upload a float array whose values are exactly representable in ``dtype``."""
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.float32))).to(device).to(dtype)
+
+
+def from_dev(t) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def bits(t) -> np.ndarray:
+    """Raw 16-bit patterns of a bf16 tensor."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def pack_rows_dev(blocks, pad=PAD, device="cuda"):
+    """Stack device bf16 blocks [r_i, K] into one [sum(pad(r_i)), K] tensor with fsvd_prepack."""
+    K = blocks[0].shape[1]
+    rp = [round_up(b.shape[0], pad) for b in blocks]
+    dst = torch.empty((sum(rp), K), dtype=blocks[0].dtype, device=device)
+    items = [(b, b.shape[0], K, b.stride(0), r) for b, r in zip(blocks, rp)]
+    fsvd.fsvd_prepack(dst, K, K, items, fsvd.dtype_of(blocks[0]))
+    return dst, rp
+
+
+def pad_cols_dev(m, cols_pad, device="cuda"):
+    """Zero-pad the columns of a device matrix [N, r] to [N, cols_pad] with fsvd_prepack."""
+    N, r = m.shape
+    dst = torch.empty((N, cols_pad), dtype=m.dtype, device=device)
+    fsvd.fsvd_prepack(dst, cols_pad, cols_pad, [(m, N, r, m.stride(0), N)], fsvd.dtype_of(m))
+    return dst
+
+
+class DeviceLayer:
+    """One Llama-style low-rank decoder layer resident on the GPU (factors packed and padded)."""
+
+    def __init__(self, cfg, p, B, S, L_max, kc, vc, seqlens, device="cuda", advance=False, x=None):
+        self.cfg, self.B, self.S, self.L_max = cfg, B, S, L_max
+        dev = device
+        up = {k: to_dev(v, device=dev) for k, v in p.items() if k.startswith(("Ut_", "Vt_"))}
+        self.A_qkv, (rq, rk, rv) = pack_rows_dev([up["Ut_q"], up["Ut_k"], up["Ut_v"]], device=dev)
+        self.Vt_q, self.Vt_k, self.Vt_v = (pad_cols_dev(up["Vt_q"], rq, dev), pad_cols_dev(up["Vt_k"], rk, dev),
+                                           pad_cols_dev(up["Vt_v"], rv, dev))
+        self.Ut_o, (ro,) = pack_rows_dev([up["Ut_o"]], device=dev)
+        self.Vt_o = pad_cols_dev(up["Vt_o"], ro, dev)
+        self.A_gu, (rg, ru) = pack_rows_dev([up["Ut_gate"], up["Ut_up"]], device=dev)
+        self.Vt_g, self.Vt_u = pad_cols_dev(up["Vt_gate"], rg, dev), pad_cols_dev(up["Vt_up"], ru, dev)
+        self.Ut_d, (rd,) = pack_rows_dev([up["Ut_down"]], device=dev)
+        self.Vt_d = pad_cols_dev(up["Vt_down"], rd, dev)
+        del up
+        self.ranks = dict(r_q=rq, r_k=rk, r_v=rv, r_o=ro, r_g=rg, r_u=ru, r_d=rd)
+        self.attn_norm_w = to_dev(p["attn_norm_w"], device=dev)
+        self.mlp_norm_w = to_dev(p["mlp_norm_w"], device=dev)
+        self.x = to_dev(p["x"] if x is None else x, device=dev).reshape(B, S, cfg.d).contiguous()
+        self.y = torch.empty_like(self.x)
+        self.k_cache = to_dev(kc, device=dev) if kc is not None else torch.zeros(
+            (B, L_max, cfg.Hkv, cfg.D), dtype=torch.bfloat16, device=dev)
+        self.v_cache = to_dev(vc, device=dev) if vc is not None else torch.zeros_like(self.k_cache)
+        self.seqlens = torch.from_numpy(np.asarray(seqlens, dtype=np.int32)).to(dev)
+        self.desc = fsvd.decoder_layer_desc(
+            B=B, S=S, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, D=cfg.D, d_ff=cfg.d_ff, L_max=L_max, **self.ranks,
+            norm_eps=cfg.norm_eps, rope_theta=cfg.rope_theta, softmax_scale=0.0, advance_seqlens=int(advance),
+            x=self.x, y=self.y, attn_norm_w=self.attn_norm_w, mlp_norm_w=self.mlp_norm_w, A_qkv=self.A_qkv,
+            Vt_q=self.Vt_q, Vt_k=self.Vt_k, Vt_v=self.Vt_v, Ut_o=self.Ut_o, Vt_o=self.Vt_o, A_gu=self.A_gu,
+            Vt_g=self.Vt_g, Vt_u=self.Vt_u, Ut_d=self.Ut_d, Vt_d=self.Vt_d, k_cache=self.k_cache,
+            v_cache=self.v_cache, cache_seqlens=self.seqlens)
+        nbytes = fsvd.fsvd_decoder_layer_ws(self.desc)
+        self.ws = fsvd.workspace(nbytes, device=dev)
+        self.desc.ws = self.ws.data_ptr()
+        self.desc.ws_bytes = self.ws.numel()
+
+    def run(self, stream=None):
+        fsvd.fsvd_decoder_layer_run(self.desc, stream)
+
+    def capture(self):
+        return fsvd.fsvd_decoder_layer_capture(self.desc)
+
+    def y_host(self):
+        return from_dev(self.y)
+
+    def factor_bytes_logical(self, p):
+        """Algorithmic factor bytes (unpadded ranks, bf16)."""
+        return 2 * sum(v.size for k, v in p.items() if k.startswith(("Ut_", "Vt_")))

@@ -1,0 +1,97 @@
+"""GPU parity of the whole decoder layer (eager and per-layer hipGraph replay) against the oracle.
+
+Graph replay changes launch overhead, not arithmetic: N replays must equal N eager steps bit
+for bit (the kernels are deterministic), and both must match the oracle's N-step composition.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import fsvd_oracle as O  # noqa: E402
+from svd_compressed_transformer_amd import fsvd, inputs as I  # noqa: E402
+from tests.layer_util import DeviceLayer, bits, from_dev, to_dev  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+BF16_TOL = 2e-2
+
+
+def rel(a, b):
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-30))
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+SMALL = I.scaled_decoder(I.CFG2, d=512, Hq=8, Hkv=8, D=64, d_ff=768,
+                         ranks={"q": 200, "k": 200, "v": 200, "o": 200, "gate": 300, "up": 300, "down": 300})
+SMALL_GQA = I.scaled_decoder(I.CFG4, d=512, Hq=8, Hkv=2, D=128, d_ff=1024,
+                             ranks={"q": 256, "k": 128, "v": 64, "o": 192, "gate": 128, "up": 256, "down": 96})
+
+
+@pytest.mark.parametrize("cfg,B,L0", [(SMALL, 1, 0), (SMALL, 3, 45), (SMALL_GQA, 4, 130), (SMALL_GQA, 32, 17)])
+def test_decode_layer_eager(cfg, B, L0):
+    L_max = 160
+    say("decode layer eager", cfg.name, B, L0)
+    p = I.make_decoder_layer(cfg, B=B, S=1, seed=B, random_norm_weights=True)
+    kc, vc = I.make_kv_history(B, L_max, cfg.Hkv, cfg.D, L0, seed=11)
+    lay = DeviceLayer(cfg, p, B=B, S=1, L_max=L_max, kc=kc, vc=vc, seqlens=np.full(B, L0))
+    lay.run()
+    torch.cuda.synchronize()
+    y_ref, kc_ref, vc_ref = O.decoder_layer(p["x"], p, cfg, kc, vc, np.full(B, L0))
+    assert rel(lay.y_host(), y_ref) <= BF16_TOL
+    assert rel(from_dev(lay.k_cache)[:, L0], kc_ref[:, L0]) <= BF16_TOL
+    assert fsvd.fsvd_poll_device_error(lay.ws) == 0
+
+
+def test_prefill_layer_small_rowdot_path():
+    """S > 1 with M = B*S <= 32 exercises the row-dot kernels with several tokens per sequence."""
+    cfg = SMALL_GQA
+    B, S, L_max = 2, 5, 64
+    say("prefill layer (row-dot sizes)")
+    p = I.make_decoder_layer(cfg, B=B, S=S, seed=21, random_norm_weights=True)
+    lay = DeviceLayer(cfg, p, B=B, S=S, L_max=L_max, kc=None, vc=None, seqlens=[0, 9])
+    lay.run()
+    torch.cuda.synchronize()
+    z = np.zeros((B, L_max, cfg.Hkv, cfg.D))
+    y_ref, _, _ = O.decoder_layer(p["x"], p, cfg, z, z, [0, 9])
+    assert rel(lay.y_host(), y_ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("cfg,B", [(SMALL, 2), (SMALL_GQA, 4)])
+def test_graph_replay_equals_eager_and_oracle(cfg, B):
+    L_max, L0, N = 96, 20, 6
+    say("graph replay", cfg.name, B)
+    p = I.make_decoder_layer(cfg, B=B, S=1, seed=5, random_norm_weights=True)
+    kc, vc = I.make_kv_history(B, L_max, cfg.Hkv, cfg.D, L0, seed=12)
+    rng = np.random.default_rng(99)
+    xs = I.round_bf16(rng.standard_normal((N, B, cfg.d)))
+
+    eager = DeviceLayer(cfg, p, B=B, S=1, L_max=L_max, kc=kc, vc=vc, seqlens=np.full(B, L0), advance=True)
+    graph_l = DeviceLayer(cfg, p, B=B, S=1, L_max=L_max, kc=kc, vc=vc, seqlens=np.full(B, L0), advance=True)
+    g = graph_l.capture()
+    try:
+        ys_e, ys_g = [], []
+        for t in range(N):
+            xt = to_dev(xs[t]).reshape(B, 1, cfg.d)
+            eager.x.copy_(xt)
+            graph_l.x.copy_(xt)
+            eager.run()
+            fsvd.fsvd_graph_replay(g)
+            torch.cuda.synchronize()
+            ys_e.append(bits(eager.y))
+            ys_g.append(bits(graph_l.y))
+        for t in range(N):
+            assert np.array_equal(ys_e[t], ys_g[t]), f"replay {t} differs from eager"
+        assert np.array_equal(bits(eager.k_cache), bits(graph_l.k_cache))
+        assert list(graph_l.seqlens.cpu().numpy()) == [L0 + N] * B
+        y_ref, _, _, sl = O.decoder_steps(xs, p, cfg, kc, vc, np.full(B, L0))
+        got = np.stack([from_dev(torch.from_numpy(y.view(np.int16)).view(torch.bfloat16)).reshape(B, cfg.d)
+                        for y in ys_g])
+        assert rel(got, y_ref) <= BF16_TOL
+    finally:
+        fsvd.fsvd_graph_destroy(g)
+    with pytest.raises(fsvd.FsvdError):
+        fsvd.fsvd_graph_replay(g)
