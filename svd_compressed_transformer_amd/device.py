@@ -1,4 +1,4 @@
-"""Device-side helpers for the GPU tests, the smoke check and the benchmark: upload host arrays,
+"""Device-side plumbing for callers of the library (tests, smoke check, benchmark): upload host arrays,
 prepack factors through the library's own fsvd_prepack, and hold one decoder layer's buffers and
 descriptor.  No arithmetic of the method lives here (and nothing here imports the oracle)."""
 from __future__ import annotations

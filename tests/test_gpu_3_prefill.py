@@ -8,7 +8,7 @@ torch = pytest.importorskip("torch")
 
 from oracle import fsvd_oracle as O  # noqa: E402
 from svd_compressed_transformer_amd import fsvd, inputs as I  # noqa: E402
-from tests.layer_util import DeviceLayer, bits, from_dev, pack_rows_dev, pad_cols_dev, to_dev  # noqa: E402
+from svd_compressed_transformer_amd.device import DeviceLayer, bits, from_dev, pack_rows_dev, pad_cols_dev, to_dev  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 BF16_TOL = 2e-2
