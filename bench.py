@@ -88,7 +88,7 @@ def cpu_baseline(cfg, budget_s=20.0):
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
     p = I.make_decoder_layer(cfg, B=1, S=256, seed=100)
-    L_max = 2048 + 64
+    L_max = 2048 + 128
     t0 = time.perf_counter()
     z = np.zeros((1, 256, cfg.Hkv, cfg.D))
     O.decoder_layer(p["x"], p, cfg, z, z, np.zeros(1, dtype=np.int64))
@@ -105,7 +105,7 @@ def cpu_baseline(cfg, budget_s=20.0):
         _, kc, vc = O.decoder_layer(x, pd, cfg, kc, vc, sl)
         sl = sl + 1
         nsteps += 1
-        if time.perf_counter() - t0 > budget_s or nsteps >= 32:
+        if time.perf_counter() - t0 > budget_s or nsteps >= 96:
             break
     t_dec = time.perf_counter() - t1
     total = t_pre + t_dec

@@ -12,7 +12,7 @@
 // that share it.  Partitions are merged by log-sum-exp in a second small kernel.  The length
 // is read on the device from cache_seqlens, so a captured graph stays valid as the cache grows.
 //
-// Sq > 1 (prefill and encoder layers) uses the same per-position streaming per query token.
+// Sq > 1 (prefill and encoder layers) runs on the matrix cores (attention_prefill.hip).
 #include "kernels.h"
 
 namespace fsvd {
@@ -152,106 +152,36 @@ __global__ __launch_bounds__(256) void attn_decode_split(const AttnArgs a) {
     }
 }
 
-// merge partitions: one workgroup per (b, h), one thread per head element
+// merge partitions: one workgroup per (b, h).  The first wave reads every partition's
+// (max, sum) at once and forms the log-sum-exp weights; then each thread owns one head element
+// and sums the weighted partial outputs (all loads independent, so one L2 round trip).
 __global__ __launch_bounds__(128) void attn_decode_combine(const AttnArgs a) {
-    const int D = a.D;
+    const int D = a.D, ns = a.nsplit;
     const int bh = blockIdx.x;
-    const int dd = threadIdx.x;
-    if (dd >= D) return;
-    const float* part = a.part + (int64_t)bh * a.nsplit * (D + 2);
-    float M = kNegBig;
-    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, part[s * (D + 2) + D]);
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < a.nsplit; ++s) {
-        const float w = exp2f(part[s * (D + 2) + D] - M);
-        L += w * part[s * (D + 2) + D + 1];
-        O += w * part[s * (D + 2) + dd];
-    }
-    a.out[(int64_t)bh * D + dd] = f2bf(O / L);
-}
-
-// Sq > 1: one workgroup per (b, query token s, kv head g); lane groups stride over positions.
-template <int EPL, int G>
-__global__ __launch_bounds__(256) void attn_prefill_rows(const AttnArgs a) {
-    const int D = EPL * 16;
-    const int tid = threadIdx.x, lg = tid >> 4, li = tid & 15;
-    const int kvh = blockIdx.x % a.Hkv;
-    const int bs = blockIdx.x / a.Hkv;
-    const int s = bs % a.Sq, b = bs / a.Sq;
-
-    int64_t n = (int64_t)a.seqlens[b] + (a.causal ? s + 1 : a.Sq);
-    if (n > a.L_max) {
-        if (tid == 0) set_dev_error(a.err, FSVD_DEVERR_SEQ_OVERFLOW);
-        n = a.L_max;
-    }
-    uint32_t qf[G][EPL / 2];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const int h = kvh * G + g;
-        const KV<EPL> v = ld_kv<EPL>(a.q + (((int64_t)b * a.Sq + s) * a.Hq + h) * D + li * EPL);
-#pragma unroll
-        for (int i = 0; i < EPL / 2; ++i) qf[g][i] = v.w[i];
-    }
-    const float sc = a.scale * kLog2e;
-    float m[G], l[G], o[G][EPL];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        m[g] = kNegBig;
-        l[g] = 0.f;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) o[g][i] = 0.f;
-    }
-    const int64_t rowstride = (int64_t)a.Hkv * D;
-    const bf16_t* kbase = a.kc + ((int64_t)b * a.L_max * a.Hkv + kvh) * D + li * EPL;
-    const bf16_t* vbase = a.vc + ((int64_t)b * a.L_max * a.Hkv + kvh) * D + li * EPL;
-    for (int64_t j = lg; j < n; j += 16) {
-        const KV<EPL> kv = ld_kv<EPL>(kbase + j * rowstride);
-        const KV<EPL> vv = ld_kv<EPL>(vbase + j * rowstride);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float d = 0.f;
-#pragma unroll
-            for (int i = 0; i < EPL / 2; ++i) d = dot2bf(qf[g][i], kv.w[i], d);
-            d = row16_sum(d) * sc;
-            const float mn = fmaxf(m[g], d);
-            const float alpha = exp2f(m[g] - mn);
-            const float pr = exp2f(d - mn);
-            m[g] = mn;
-            l[g] = l[g] * alpha + pr;
-#pragma unroll
-            for (int i = 0; i < EPL / 2; ++i) {
-                o[g][2 * i] = o[g][2 * i] * alpha + pr * bf_lo(vv.w[i]);
-                o[g][2 * i + 1] = o[g][2 * i + 1] * alpha + pr * bf_hi(vv.w[i]);
-            }
-        }
-    }
-    __shared__ float sm[16 * G * (16 * EPL + 2)];
-    const int stride = D + 2;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        float* row = sm + (lg * G + g) * stride;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) row[li * EPL + i] = o[g][i];
-        if (li == 0) {
-            row[D] = m[g];
-            row[D + 1] = l[g];
-        }
+    const int t = threadIdx.x;
+    const float* part = a.part + (int64_t)bh * ns * (D + 2);
+    __shared__ float w[64];
+    __shared__ float inv_l;
+    if (t < 64) {
+        const bool ok = t < ns;
+        const float ms = ok ? part[t * (D + 2) + D] : kNegBig;
+        const float ls = ok ? part[t * (D + 2) + D + 1] : 0.f;
+        float M = row16_max(ms);
+        M = fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, M), 0)),
+                        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, M), 16))),
+                  fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, M), 32)),
+                        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, M), 48))));
+        const float ws = ok ? exp2f(ms - M) : 0.f;
+        w[t] = ws;
+        const float L = wave_sum(ws * ls);
+        if (t == 0) inv_l = 1.0f / L;
     }
     __syncthreads();
-    for (int idx = tid; idx < G * D; idx += 256) {
-        const int g = idx / D, dd = idx - g * D;
-        float M = kNegBig;
-        for (int q = 0; q < 16; ++q) M = fmaxf(M, sm[(q * G + g) * stride + D]);
-        float L = 0.f, O = 0.f;
-        for (int q = 0; q < 16; ++q) {
-            const float* row = sm + (q * G + g) * stride;
-            const float w = exp2f(row[D] - M);
-            L += w * row[D + 1];
-            O += w * row[dd];
-        }
-        const int h = kvh * G + g;
-        a.out[(((int64_t)b * a.Sq + s) * a.Hq + h) * D + dd] = f2bf(O / L);
-    }
+    if (t >= D) return;
+    float O = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < ns; ++s) O += w[s] * part[s * (D + 2) + t];
+    a.out[(int64_t)bh * D + t] = f2bf(O * inv_l);
 }
 
 template <int EPL>
@@ -271,20 +201,6 @@ fsvd_status_t launch_decode_d(const AttnArgs& a, hipStream_t st) {
     return check_launch("attn_decode_combine");
 }
 
-template <int EPL>
-fsvd_status_t launch_prefill_d(const AttnArgs& a, hipStream_t st) {
-    const int G = a.Hq / a.Hkv;
-    const int grid = a.B * a.Sq * a.Hkv;
-    switch (G) {
-        case 1: attn_prefill_rows<EPL, 1><<<grid, 256, 0, st>>>(a); break;
-        case 2: attn_prefill_rows<EPL, 2><<<grid, 256, 0, st>>>(a); break;
-        case 4: attn_prefill_rows<EPL, 4><<<grid, 256, 0, st>>>(a); break;
-        case 8: attn_prefill_rows<EPL, 8><<<grid, 256, 0, st>>>(a); break;
-        default: return fail(FSVD_ERR_UNSUPPORTED, "GQA group size %d not in {1,2,4,8}", G);
-    }
-    return check_launch("attn_prefill_rows");
-}
-
 }  // namespace
 
 size_t attn_decode_ws_bytes(int B, int Hq, int D, int nsplit) {
@@ -302,12 +218,6 @@ int attn_default_splits(int B, int Hkv, int64_t L_max) {
 fsvd_status_t launch_attn_decode(const AttnArgs& a, hipStream_t st) {
     if (a.D == 128) return launch_decode_d<8>(a, st);
     if (a.D == 64) return launch_decode_d<4>(a, st);
-    return fail(FSVD_ERR_UNSUPPORTED, "head dim %d not in {64,128}", a.D);
-}
-
-fsvd_status_t launch_attn_prefill(const AttnArgs& a, hipStream_t st) {
-    if (a.D == 128) return launch_prefill_d<8>(a, st);
-    if (a.D == 64) return launch_prefill_d<4>(a, st);
     return fail(FSVD_ERR_UNSUPPORTED, "head dim %d not in {64,128}", a.D);
 }
 

@@ -35,7 +35,8 @@ struct RowdotSeg {
 struct RowdotArgs {
     RowdotSeg seg[3];
     int nseg;
-    int ksplit;      // waves sharing one row group (split of the reduction), 1, 2 or 4
+    int ksplit;      // waves sharing one row group (split of the reduction): 1, 2, 4 or 8
+    int waves;       // waves per workgroup: 4 or 8
     const void* act; // [M, lda]
     int64_t lda;
     int M;

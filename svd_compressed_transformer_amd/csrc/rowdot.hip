@@ -6,8 +6,10 @@
 // activation rows.  A wave owns R rows; each lane loads 16 contiguous bytes of every row per
 // step (one wave instruction = a 1 KiB coalesced segment of each row), multiplies them with the
 // matching activation bytes using v_dot2_f32_bf16 (fp32 accumulation), and the 64 lanes are
-// reduced with DPP row operations plus a small LDS combine.  Long reductions are split over
-// the waves of a workgroup so the grid has enough waves in flight to cover HBM latency.
+// reduced with DPP row operations plus a small LDS combine.  Measured on MI355X, these streams are
+// bound by how many bytes are in flight and by the activation re-reads, not by arithmetic: a wave
+// owns 4 rows (each activation load feeds 4 rows), issues its loads in passes of 1-4 steps, and
+// long reductions are split over the 4-8 waves of a workgroup, giving thousands of short waves.
 //
 // Phase 1 (z = a . Ut^T, EPI_Z) fuses the RMSNorm prologue: the sum of squares of each
 // activation row is accumulated in the same pass and z is scaled by rstd at the end.  Phase 2
@@ -24,9 +26,12 @@ namespace fsvd {
 
 namespace {
 
-constexpr int kR = 4;       // factor rows per wave
-constexpr int kWaves = 4;   // waves per workgroup
-constexpr int kUnroll = 2;  // 16-byte steps issued before use
+#ifndef FSVD_ROWS
+#define FSVD_ROWS 4
+#endif
+constexpr int kR = FSVD_ROWS;  // factor rows per wave (even)
+constexpr int kH = kR / 2;     // paired units per wave
+constexpr int kMaxWaves = 8; // waves per workgroup (4 or 8, chosen per launch)
 
 template <typename T>
 struct Vec;
@@ -40,6 +45,18 @@ struct Vec<float> {
 };
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// factor bytes are read exactly once: stream them past the caches so the activation rows, which
+// every wave re-reads, stay resident
+#ifndef FSVD_WEIGHT_NT
+#define FSVD_WEIGHT_NT 1
+#endif
+__device__ __forceinline__ u32x4 ldg16_stream(const void* p) {
+#if FSVD_WEIGHT_NT
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+    return *reinterpret_cast<const u32x4*>(p);
+#endif
+}
 
 __device__ __forceinline__ float vdot(u32x4 w, u32x4 a, float c, bf16_t) {
     c = dot2bf(w.x, a.x, c);
@@ -104,7 +121,7 @@ __host__ __device__ __forceinline__ bool seg_paired(int epi, int kind) {
 }
 
 template <typename T, int BMAX, int EPI>
-__global__ __launch_bounds__(256) void rowdot_kernel(const RowdotArgs a) {
+__global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const RowdotArgs a) {
     constexpr int E = Vec<T>::E;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bid = blockIdx.x;
@@ -113,14 +130,15 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const RowdotArgs a) {
     const RowdotSeg sg = si == 0 ? a.seg[0] : (si == 1 ? a.seg[1] : a.seg[2]);
 
     const bool paired = seg_paired(EPI, sg.kind);
-    const int upw = paired ? kR / 2 : kR;                        // output units per wave
+    const int upw = paired ? kH : kR;                             // output units per wave
     const int n_units = (EPI == EPI_QKV && paired) ? sg.N / 2 : sg.N;
     const int ksplit = a.ksplit;
     const int grp = wave / ksplit, ks = wave - grp * ksplit;
     const int unit0 = (bid - sg.blk_begin) * sg.units_per_blk + grp * upw;
     const int halfD = a.D >> 1;
 
-    // rows owned by this wave
+    // rows owned by this wave: paired units (RoPE pair, or gate/up of one column) use both rows
+    // for one output unit; plain segments give each row its own unit
     const char* wrow[kR];
     int klen[kR];
     int aoff[kR];
@@ -128,13 +146,13 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const RowdotArgs a) {
     for (int r = 0; r < kR; ++r) {
         int u, n, mat = 0;
         if (paired) {
-            u = unit0 + (r & 1);
+            u = unit0 + r % kH;
             if (EPI == EPI_SWIGLU) {
-                mat = r >> 1;
+                mat = r / kH;
                 n = u;
             } else {
                 const int h = u / halfD, i = u - h * halfD;
-                n = h * a.D + i + (r >> 1) * halfD;
+                n = h * a.D + i + (r / kH) * halfD;
             }
         } else {
             u = unit0 + r;
@@ -167,49 +185,56 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const RowdotArgs a) {
     const bool norm = (EPI == EPI_Z) && a.norm;
     const bool norm_w = norm && a.norm_w != nullptr;
 
-    for (int kb = k_lo; kb < k_hi; kb += 64 * E * kUnroll) {
-        u32x4 wv[kUnroll][kR];
+    // One pass per U steps: every W and activation load of the pass is issued before the first
+    // product (predicated, branch-free), so a wave waits for HBM once per pass.
+    constexpr int U = BMAX <= 2 ? 4 : (BMAX <= 8 ? 2 : 1);
+    constexpr int NA = EPI == EPI_SWIGLU ? 2 : 1;  // distinct activation vectors (gate, up)
+    const int ka0 = EPI == EPI_SWIGLU ? sg.K : k_hi, ka1 = EPI == EPI_SWIGLU ? sg.K2 : k_hi;
+    for (int kb = k_lo; kb < k_hi; kb += 64 * E * U) {
+        u32x4 wv[U][kR];
+        u32x4 av[U][BMAX][NA];
+        u32x4 nw[U];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int k = kb + (u * 64 + lane) * E;
+            const bool in = k < k_hi;
 #pragma unroll
-            for (int r = 0; r < kR; ++r) {
-                if (k < k_hi && k < klen[r])
-                    wv[u][r] = ldg16(wrow[r] + (int64_t)k * sizeof(T));
-                else
-                    wv[u][r] = u32x4{0u, 0u, 0u, 0u};
+            for (int r = 0; r < kR; ++r)
+                wv[u][r] = (in && k < klen[r]) ? ldg16_stream(wrow[r] + (int64_t)k * sizeof(T)) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = kb + (u * 64 + lane) * E;
+            const bool in = k < k_hi;
+            nw[u] = (norm_w && in) ? ldg16(a.norm_w + k) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int b = 0; b < BMAX; ++b) {
+#pragma unroll
+                for (int x = 0; x < NA; ++x) {
+                    const int off = x ? aoff[kH] : aoff[0];
+                    const bool ok = b < M && in && k < (x ? ka1 : ka0);
+                    av[u][b][x] = ok ? ldg16(act + b * lda_b + (int64_t)(off + k) * sizeof(T)) : u32x4{0u, 0u, 0u, 0u};
+                }
             }
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int k = kb + (u * 64 + lane) * E;
-            if (k >= k_hi) continue;
-            u32x4 nw = u32x4{0u, 0u, 0u, 0u};
-            if (norm_w) nw = ldg16(a.norm_w + k);
+        for (int u = 0; u < U; ++u) {
 #pragma unroll
             for (int b = 0; b < BMAX; ++b) {
                 if (b >= M) continue;
-                if (EPI == EPI_SWIGLU) {
-                    if (k < sg.K) {
-                        const u32x4 av = ldg16(act + b * lda_b + (int64_t)(aoff[0] + k) * sizeof(T));
-                        acc[0][b] = vdot(wv[u][0], av, acc[0][b], T());
-                        acc[1][b] = vdot(wv[u][1], av, acc[1][b], T());
-                    }
-                    if (k < sg.K2) {
-                        const u32x4 av = ldg16(act + b * lda_b + (int64_t)(aoff[2] + k) * sizeof(T));
-                        acc[2][b] = vdot(wv[u][2], av, acc[2][b], T());
-                        acc[3][b] = vdot(wv[u][3], av, acc[3][b], T());
-                    }
+                if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+                    for (int r = 0; r < kR; ++r) acc[r][b] = vdot(wv[u][r], av[u][b][r / kH], acc[r][b], T());
                 } else {
-                    u32x4 av = ldg16(act + b * lda_b + (int64_t)(aoff[0] + k) * sizeof(T));
+                    u32x4 x = av[u][b][0];
                     if constexpr (EPI == EPI_Z) {
                         if (norm) {
-                            ss[b] += vsq(av, T());
-                            if (norm_w) av = vmulw(av, nw);
+                            ss[b] += vsq(x, T());
+                            if (norm_w) x = vmulw(x, nw[u]);
                         }
                     }
 #pragma unroll
-                    for (int r = 0; r < kR; ++r) acc[r][b] = vdot(wv[u][r], av, acc[r][b], T());
+                    for (int r = 0; r < kR; ++r) acc[r][b] = vdot(wv[u][r], x, acc[r][b], T());
                 }
             }
         }
@@ -217,7 +242,7 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const RowdotArgs a) {
 
     // lanes -> 4 row partials per value (DPP), then waves/rows combined through LDS
     constexpr int NV = (kR + 1) * BMAX;
-    __shared__ float red[kWaves][4][NV];
+    __shared__ float red[kMaxWaves][4][NV];
 #pragma unroll
     for (int b = 0; b < BMAX; ++b) {
         if (b >= M) continue;
@@ -244,9 +269,9 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const RowdotArgs a) {
         return s;
     };
 
-    const int ngroups = kWaves / ksplit;
+    const int ngroups = a.waves / ksplit;
     const int total = ngroups * upw * M;
-    for (int idx = tid; idx < total; idx += 256) {
+    for (int idx = tid; idx < total; idx += 64 * a.waves) {
         const int g = idx / (upw * M);
         const int rem = idx - g * upw * M;
         const int j = rem / M;           // unit within the wave
@@ -268,7 +293,7 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const RowdotArgs a) {
         } else if constexpr (EPI == EPI_GELU) {
             store_t<T>(sg.out, (int64_t)m * sg.ldo + u, gelu_f(val(g, j, m)));
         } else if constexpr (EPI == EPI_SWIGLU) {
-            const float gv = val(g, j, m), uv = val(g, j + 2, m);
+            const float gv = val(g, j, m), uv = val(g, j + kH, m);
             store_t<T>(sg.out, (int64_t)m * sg.ldo + u, silu_f(gv) * uv);
         } else if constexpr (EPI == EPI_QKV) {
             const int b = m / a.S, s = m - b * a.S;
@@ -281,7 +306,7 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const RowdotArgs a) {
                 else set_dev_error(a.err, FSVD_DEVERR_KV_OVERFLOW);
                 if (a.v_out) a.v_out[(int64_t)m * hd + u] = bits;
             } else {
-                const float x1 = val(g, j, m), x2 = val(g, j + 2, m);
+                const float x1 = val(g, j, m), x2 = val(g, j + kH, m);
                 const int h = u / halfD, i = u - h * halfD;
                 const int n1 = h * a.D + i, n2 = n1 + halfD;
                 float y1 = x1, y2 = x2;
@@ -318,44 +343,44 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const RowdotArgs a) {
 template <typename T, int EPI>
 fsvd_status_t launch_b(const RowdotArgs& a, int grid, hipStream_t st) {
     const int M = a.M;
-    if (M <= 1) rowdot_kernel<T, 1, EPI><<<grid, 256, 0, st>>>(a);
-    else if (M <= 2) rowdot_kernel<T, 2, EPI><<<grid, 256, 0, st>>>(a);
-    else if (M <= 4) rowdot_kernel<T, 4, EPI><<<grid, 256, 0, st>>>(a);
-    else if (M <= 8) rowdot_kernel<T, 8, EPI><<<grid, 256, 0, st>>>(a);
-    else if (M <= 16) rowdot_kernel<T, 16, EPI><<<grid, 256, 0, st>>>(a);
-    else rowdot_kernel<T, 32, EPI><<<grid, 256, 0, st>>>(a);
+    if (M <= 1) rowdot_kernel<T, 1, EPI><<<grid, 64 * a.waves, 0, st>>>(a);
+    else if (M <= 2) rowdot_kernel<T, 2, EPI><<<grid, 64 * a.waves, 0, st>>>(a);
+    else if (M <= 4) rowdot_kernel<T, 4, EPI><<<grid, 64 * a.waves, 0, st>>>(a);
+    else if (M <= 8) rowdot_kernel<T, 8, EPI><<<grid, 64 * a.waves, 0, st>>>(a);
+    else if (M <= 16) rowdot_kernel<T, 16, EPI><<<grid, 64 * a.waves, 0, st>>>(a);
+    else rowdot_kernel<T, 32, EPI><<<grid, 64 * a.waves, 0, st>>>(a);
     return check_launch("rowdot");
 }
 
 }  // namespace
 
 int rowdot_plan(RowdotArgs& a, int epi) {
-    // pick the reduction split so the grid has enough waves, then lay segments out
-    int ksplit = 1;
-    for (;;) {
-        int blocks = 0, kmax = 0;
-        for (int i = 0; i < a.nseg; ++i) {
-            const RowdotSeg& s = a.seg[i];
-            const bool paired = seg_paired(epi, s.kind);
-            const int upw = paired ? kR / 2 : kR;
-            const int units = (epi == EPI_QKV && paired) ? s.N / 2 : s.N;
-            const int upb = (kWaves / ksplit) * upw;
-            blocks += (units + upb - 1) / upb;
-            kmax = std::max(kmax, std::max(s.K, epi == EPI_SWIGLU ? s.K2 : 0));
-        }
-        if (blocks >= 600 || ksplit == 4 || kmax / (ksplit * 2) < 512) break;
-        ksplit *= 2;
+    // Reduction split: about 1024 elements per wave for long reductions (one or two load passes),
+    // then doubled while the launch has fewer than ~2048 waves.  4 waves per workgroup, 8 when the
+    // split needs them.
+    int kmax = 0, units = 0;
+    for (int i = 0; i < a.nseg; ++i) {
+        const RowdotSeg& s = a.seg[i];
+        const bool paired = seg_paired(epi, s.kind);
+        kmax = std::max(kmax, std::max(s.K, epi == EPI_SWIGLU ? s.K2 : 0));
+        const int u = (epi == EPI_QKV && paired) ? s.N / 2 : s.N;
+        units += paired ? (u + kH - 1) / kH : (u + kR - 1) / kR;  // row groups
     }
+    int ksplit = 1;
+    while (ksplit < 8 && (kmax + ksplit - 1) / ksplit > 1024 && kmax / (ksplit * 2) >= 256) ksplit *= 2;
+    while (ksplit < 8 && (int64_t)units * ksplit < 2048 && kmax / (ksplit * 2) >= 256) ksplit *= 2;
+    if (a.M > 16) ksplit = std::min(ksplit, 4);  // the 32-row variant runs 4-wave workgroups
     a.ksplit = ksplit;
+    a.waves = ksplit > 4 ? 8 : 4;
     int blk = 0;
     for (int i = 0; i < a.nseg; ++i) {
         RowdotSeg& s = a.seg[i];
         const bool paired = seg_paired(epi, s.kind);
-        const int upw = paired ? kR / 2 : kR;
-        const int units = (epi == EPI_QKV && paired) ? s.N / 2 : s.N;
-        s.units_per_blk = (kWaves / ksplit) * upw;
+        const int upw = paired ? kH : kR;
+        const int n_units = (epi == EPI_QKV && paired) ? s.N / 2 : s.N;
+        s.units_per_blk = (a.waves / ksplit) * upw;
         s.blk_begin = blk;
-        blk += (units + s.units_per_blk - 1) / s.units_per_blk;
+        blk += (n_units + s.units_per_blk - 1) / s.units_per_blk;
     }
     return blk;
 }
