@@ -5,9 +5,10 @@
 // NT GEMM C[M, N] = A[M, K] . B[N, K]^T on the matrix cores with a fused epilogue:
 //   - tiles of BM x BN (256 or 128 x 256 or 128), BK = 64, four waves as 2 x 2, each wave a grid
 //     of 32 x 32 blocks computed with v_mfma_f32_32x32x16_bf16 (fp32 accumulation);
-//   - operands staged global -> registers -> LDS, double buffered, in an XOR-swizzled layout
-//     (16-byte chunk c of row r stored at chunk c ^ (r & 7)) so the 32-row fragment reads of one
-//     MFMA hit distinct banks; M/N/K tails are zero-filled;
+//   - operands move global -> LDS directly (global_load_lds_dwordx4, no staging registers) through
+//     a 4-stage pipeline of BK = 32 slices, each lane choosing the global chunk whose XOR-swizzled
+//     LDS home is its slot, so the 32-row fragment reads of one MFMA hit distinct banks; M/N tails
+//     re-read the last row (never stored), the K tail is zeroed in LDS;
 //   - tiles are handed out XCD by XCD (workgroup i runs on XCD i mod 8) so the WGs that share an
 //     XCD's L2 work on neighbouring M tiles of one N tile and reuse its B operand.
 // Epilogues: per-row scale (RMSNorm folded after the product), bias + residual, Q/K/V with
@@ -26,39 +27,87 @@ namespace {
 typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BK = 64;          // k per LDS stage (8 chunks of 16 bytes per row)
+constexpr int BK = 32;          // k per LDS stage: 4 chunks of 16 bytes per row
+constexpr int kStages = 4;      // LDS pipeline depth
 constexpr int kThreads = 256;   // 4 waves, arranged 2 x 2
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+typedef __attribute__((address_space(3))) void lds_void;
 
-// global -> register staging of one operand tile (ROWS x BK); zero outside [0,rows) x [0,K)
+// chunk c of row r of a stage buffer sits at chunk slot r * 4 + (c ^ ((r >> 2) & 3)): the 16 rows
+// read by one quarter-wave for an MFMA fragment then fall in 16 distinct 16-byte bank groups
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 4 + (chunk ^ ((row >> 2) & 3)); }
+
+// Issue the direct global -> LDS loads of one operand tile (ROWS x BK) into stage buffer 'dst'.
+// A wave instruction writes 64 consecutive 16-byte slots; each lane picks the global chunk whose
+// swizzled home is its slot.  Rows past 'rows' re-read the last row (their products are never
+// stored); chunks past K are clamped inside the row and zeroed by zero_k_tail() before use.
 template <int ROWS>
-struct Stage {
-    static constexpr int N = ROWS * 8 / kThreads;  // 16-byte chunks per thread
-    u32x4 v[N];
-    __device__ __forceinline__ void load(const bf16_t* base, int64_t ld, int row0, int rows, int k0, int K, int tid) {
+__device__ __forceinline__ void issue_tile(const bf16_t* base, int64_t ld, int row0, int rows, int k0, int K,
+                                           u32x4* dst, int wave, int lane) {
+    constexpr int PER_WAVE = ROWS * 4 / 64 / 4;  // instructions per wave
 #pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const int q = tid + i * kThreads;
-            const int r = q >> 3, c = q & 7;
-            const int gr = row0 + r, gk = k0 + c * 8;
-            if (gr < rows && gk < K)
-                v[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)gr * ld + gk);
-            else
-                v[i] = u32x4{0u, 0u, 0u, 0u};
-        }
+    for (int i = 0; i < PER_WAVE; ++i) {
+        const int slot0 = (wave * PER_WAVE + i) * 64;
+        const int slot = slot0 + lane;
+        const int r = slot >> 2, phys = slot & 3;
+        const int c = phys ^ ((r >> 2) & 3);
+        const int gr = min(row0 + r, rows - 1);
+        const int gk = min(k0 + c * 8, K - 8);
+        __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)gr * ld + gk), (lds_void*)(dst + slot0), 16, 0, 0);
     }
-    __device__ __forceinline__ void store(u32x4* lds, int tid) const {
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const int q = tid + i * kThreads;
-            lds[swz(q >> 3, q & 7)] = v[i];
-        }
+}
+
+// zero the chunks of a stage whose k index is >= K (only the last k tile can have them)
+template <int ROWS>
+__device__ __forceinline__ void zero_k_tail(u32x4* dst, int k0, int K, int tid) {
+    for (int q = tid; q < ROWS * 4; q += kThreads) {
+        const int r = q >> 2, c = q & 3;
+        if (k0 + c * 8 >= K) dst[swz(r, c)] = u32x4{0u, 0u, 0u, 0u};
     }
-};
+}
 
 __device__ __forceinline__ bf16x8_v frag(const u32x4* lds, int row, int chunk) {
     return __builtin_bit_cast(bf16x8_v, lds[swz(row, chunk)]);
+}
+
+// s_waitcnt on the vector-memory counter only: vmcnt in bits [3:0] and [15:14], expcnt (bits 6:4)
+// and lgkmcnt (bits 11:8) left at their maxima so they do not wait
+#define FSVD_VMCNT(n) (0x0F70 | ((n) & 0xF) | ((((n) >> 4) & 3) << 14))
+__device__ __forceinline__ void wait_vm(int n) {
+    // wait until at most n vector-memory operations of this wave are outstanding (n rounded down)
+    if (n >= 16) __builtin_amdgcn_s_waitcnt(FSVD_VMCNT(16));
+    else if (n >= 12) __builtin_amdgcn_s_waitcnt(FSVD_VMCNT(12));
+    else if (n >= 8) __builtin_amdgcn_s_waitcnt(FSVD_VMCNT(8));
+    else if (n >= 6) __builtin_amdgcn_s_waitcnt(FSVD_VMCNT(6));
+    else __builtin_amdgcn_s_waitcnt(FSVD_VMCNT(0));
+}
+
+// Workgroup barrier that waits for this wave's LDS operations only.  __syncthreads() would also
+// drain every outstanding global load (vmcnt(0)), i.e. the prefetches of later stages, which is
+// exactly what the pipeline must keep in flight; stage arrival is ordered by wait_vm() instead.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt unchanged
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Instruction order for one pipeline phase of NM MFMAs: the NR LDS reads and the NG global loads
+// issued in that phase are spread evenly between the MFMAs (reads first), so they issue in the
+// shadow of the matrix cores instead of in a burst that stalls them.
+template <int NR, int NG, int NM, int Q = 0>
+__device__ __forceinline__ void sched_interleave() {
+    constexpr int NX = NG + NR;
+    constexpr int per = NX ? (NM + NX - 1) / NX : NM;  // MFMAs between two memory instructions
+    constexpr int left = NM - Q * per > 0 ? NM - Q * per : 0;
+    constexpr int m = left < per ? left : per;
+    if constexpr (Q < NX) {
+        if constexpr (m > 0) __builtin_amdgcn_sched_group_barrier(0x008, m, 0);
+        __builtin_amdgcn_sched_group_barrier(Q < NR ? 0x100 : 0x020, 1, 0);
+        sched_interleave<NR, NG, NM, Q + 1>();
+    } else if constexpr (left > 0) {
+        __builtin_amdgcn_sched_group_barrier(0x008, left, 0);
+    }
 }
 
 // C tile accumulation over k in [0, K): acc[i][j] += A[wm + 32 i + .., k] . B[wn + 32 j + .., k]
@@ -66,6 +115,8 @@ template <int BM, int BN>
 struct Tile {
     static constexpr int WM = BM / 2, WN = BN / 2;      // wave tile
     static constexpr int FI = WM / 32, FJ = WN / 32;    // 32x32 blocks per wave
+    static constexpr int STAGE = (BM + BN) * 4;         // 16-byte slots per stage
+    static constexpr int LOADS = (BM + BN) * 4 / 64 / 4;  // load instructions per wave per stage
     f32x16 acc[FI][FJ];
 
     __device__ __forceinline__ void zero() {
@@ -77,71 +128,133 @@ struct Tile {
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
     }
 
+    // fragments of one 16-wide k step (substep kk of a BK = 32 stage) for this wave
+    __device__ __forceinline__ void read_frags(const u32x4* st, int kk, int wm, int wn, int lane, bf16x8_v (&af)[FI],
+                                               bf16x8_v (&bf)[FJ]) {
+        const u32x4* pa = st;
+        const u32x4* pb = st + BM * 4;
+        const int ch = kk * 2 + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < FI; ++i) af[i] = frag(pa, wm + i * 32 + (lane & 31), ch);
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) bf[j] = frag(pb, wn + j * 32 + (lane & 31), ch);
+    }
+
+    __device__ __forceinline__ void mfmas(const bf16x8_v (&af)[FI], const bf16x8_v (&bf)[FJ]) {
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+            for (int j = 0; j < FJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+
+    // Software pipeline over k tiles, two 16-wide substeps per tile.  Global -> LDS loads run
+    // three tiles ahead; within a tile, the fragments of the next substep are read from LDS while
+    // the MFMAs of the current one run, so the matrix cores wait neither for LDS nor at the single
+    // barrier per tile, which sits between the two substeps:
+    //   [loads of tile kt+3] [reads F1(kt)] [MFMA F0(kt)] wait tile kt+1, barrier
+    //   [reads F0(kt+1)] [MFMA F1(kt)]
+    // The barrier makes tile kt+1 visible and retires every wave's reads of tile kt, whose stage
+    // the next iteration's loads (tile kt+4) overwrite.
     __device__ __forceinline__ void run(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ldb, int m0, int n0,
                                         int M, int N, int K, u32x4* smem, int tid) {
         const int lane = tid & 63, wave = tid >> 6;
         const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
-        u32x4* la[2] = {smem, smem + BM * 8 + BN * 8};
-        u32x4* lb[2] = {smem + BM * 8, smem + 2 * BM * 8 + BN * 8};
-        Stage<BM> sa;
-        Stage<BN> sb;
         const int nk = (K + BK - 1) / BK;
-        sa.load(A, lda, m0, M, 0, K, tid);
-        sb.load(B, ldb, n0, N, 0, K, tid);
-        sa.store(la[0], tid);
-        sb.store(lb[0], tid);
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            const int cur = kt & 1;
-            if (kt + 1 < nk) {
-                sa.load(A, lda, m0, M, (kt + 1) * BK, K, tid);
-                sb.load(B, ldb, n0, N, (kt + 1) * BK, K, tid);
+        auto issue = [&](int t) {
+            u32x4* st = smem + (t % kStages) * STAGE;
+            issue_tile<BM>(A, lda, m0, M, t * BK, K, st, wave, lane);
+            issue_tile<BN>(B, ldb, n0, N, t * BK, K, st + BM * 4, wave, lane);
+        };
+        // the last tile's chunks past K are zeroed once it has landed (all waves), before any read
+        auto k_tail = [&](int t) {
+            if (t == nk - 1 && K % BK) {
+                lds_barrier();
+                u32x4* st = smem + (t % kStages) * STAGE;
+                zero_k_tail<BM>(st, t * BK, K, tid);
+                zero_k_tail<BN>(st + BM * 4, t * BK, K, tid);
             }
-            const u32x4* pa = la[cur];
-            const u32x4* pb = lb[cur];
-#pragma unroll
-            for (int kk = 0; kk < BK / 16; ++kk) {
-                const int ch = kk * 2 + (lane >> 5);
-                bf16x8_v af[FI], bfr[FJ];
-#pragma unroll
-                for (int i = 0; i < FI; ++i) af[i] = frag(pa, wm + i * 32 + (lane & 31), ch);
-#pragma unroll
-                for (int j = 0; j < FJ; ++j) bfr[j] = frag(pb, wn + j * 32 + (lane & 31), ch);
-#pragma unroll
-                for (int i = 0; i < FI; ++i)
-#pragma unroll
-                    for (int j = 0; j < FJ; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-            }
-            if (kt + 1 < nk) {
-                sa.store(la[cur ^ 1], tid);
-                sb.store(lb[cur ^ 1], tid);
-            }
-            __syncthreads();
+        };
+        bf16x8_v a0[FI], b0[FJ], a1[FI], b1[FJ];
+        // prologue: tiles 0 .. 2 in flight, tile 0 landed, F0(0) read
+        const int pro = min(nk, kStages - 1);
+        for (int t = 0; t < pro; ++t) issue(t);
+        wait_vm((pro - 1) * LOADS);
+        k_tail(0);
+        lds_barrier();
+        read_frags(smem, 0, wm, wn, lane, a0, b0);
+
+        // steady state: every iteration issues tile kt + 3, so tiles kt+2 and kt+3 may still be
+        // in flight when tile kt+1 must have landed
+        int kt = 0;
+        for (; kt + kStages - 1 < nk; ++kt) {
+            // phase A: loads of tile kt+3 and reads of F1(kt) interleaved with the MFMAs of F0(kt)
+            __builtin_amdgcn_sched_barrier(0);
+            const u32x4* st = smem + (kt % kStages) * STAGE;
+            read_frags(st, 1, wm, wn, lane, a1, b1);
+            issue(kt + kStages - 1);
+            mfmas(a0, b0);
+            sched_interleave<FI + FJ, 2 * LOADS, FI * FJ>();
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vm((kStages - 2) * LOADS);
+            lds_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            // phase B: reads of F0(kt+1) interleaved with the MFMAs of F1(kt)
+            read_frags(smem + ((kt + 1) % kStages) * STAGE, 0, wm, wn, lane, a0, b0);
+            mfmas(a1, b1);
+            sched_interleave<FI + FJ, 0, FI * FJ>();
+            __builtin_amdgcn_sched_barrier(0);
         }
+        // drain: no more loads to issue
+        for (; kt < nk; ++kt) {
+            const u32x4* st = smem + (kt % kStages) * STAGE;
+            read_frags(st, 1, wm, wn, lane, a1, b1);
+            mfmas(a0, b0);
+            if (kt + 1 < nk) {
+                wait_vm((nk - 2 - kt) * LOADS);
+                k_tail(kt + 1);
+                lds_barrier();
+                read_frags(smem + ((kt + 1) % kStages) * STAGE, 0, wm, wn, lane, a0, b0);
+            }
+            mfmas(a1, b1);
+        }
+        __syncthreads();  // the caller may reuse the stage buffers
     }
 };
 
-// tile index -> (m tile, n tile), XCD-grouped: workgroup i runs on XCD i % 8
+// workgroup -> (m tile, n tile).  Workgroup i runs on XCD i % 8; each XCD receives a contiguous
+// range of logical tiles, and logical tiles are ordered in groups of GM m-tiles walked column by
+// column, so the ~32 workgroups an XCD runs at once cover a GM x (32 / GM) patch of C and share
+// GM A panels and 32 / GM B panels through that XCD's L2.
+template <int GM>
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int* tm, int* tn) {
     const int nt = tiles_m * tiles_n;
     const int bid = blockIdx.x;
     const int per = (nt + 7) / 8;
     const int full = nt - 8 * (per - 1);  // XCDs that receive 'per' tiles (the rest get per - 1)
     const int x = bid & 7, local = bid >> 3;
-    const int logical = (x < full) ? x * per + local : full * per + (x - full) * (per - 1) + local;
-    *tn = logical / tiles_m;
-    *tm = logical - *tn * tiles_m;
+    const int L = (x < full) ? x * per + local : full * per + (x - full) * (per - 1) + local;
+    const int in_group = GM * tiles_n;
+    const int group = L / in_group;
+    const int first_m = group * GM;
+    const int gsize = min(tiles_m - first_m, GM);
+    const int r = L - group * in_group;
+    *tm = first_m + r % gsize;
+    *tn = r / gsize;
 }
 
 template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
+__global__ __launch_bounds__(kThreads, 1)
+#if defined(FSVD_GEMM_WPE)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+#endif
+void gemm_kernel(const GemmArgs g) {
     extern __shared__ u32x4 smem[];
     using T = Tile<BM, BN>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
     int tm, tn;
-    tile_coords(tiles_m, tiles_n, &tm, &tn);
+    tile_coords<(BM >= 256 ? 4 : 8)>(tiles_m, tiles_n, &tm, &tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
     T t;
@@ -247,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
 template <int BM, int BN, int EPI>
 fsvd_status_t launch_t(const GemmArgs& g, hipStream_t st) {
     const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-    const size_t lds = (size_t)2 * (BM + BN) * BK * 2;
+    const size_t lds = (size_t)kStages * (BM + BN) * BK * 2;
     static bool attr_set = false;
     if (!attr_set) {
         (void)hipFuncSetAttribute((const void*)gemm_kernel<BM, BN, EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
