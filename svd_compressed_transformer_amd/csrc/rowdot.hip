@@ -116,9 +116,13 @@ __device__ __forceinline__ float load_t<float>(const void* base, int64_t idx) {
     return reinterpret_cast<const float*>(base)[idx];
 }
 
+// Q and K rows are owned in RoPE pairs (both rows of a pair in one wave, one output unit)
 __host__ __device__ __forceinline__ bool seg_paired(int epi, int kind) {
-    return (epi == EPI_QKV && (kind == SEG_Q || kind == SEG_K)) || epi == EPI_SWIGLU;
+    return epi == EPI_QKV && (kind == SEG_Q || kind == SEG_K);
 }
+// SwiGLU: the gate rows and the up rows of the same kR output columns are owned by two sibling
+// wave sets (each wave reads one activation vector, z_gate or z_up), joined in the LDS combine
+__host__ __device__ __forceinline__ int wave_sets(int epi) { return epi == EPI_SWIGLU ? 2 : 1; }
 
 template <typename T, int BMAX, int EPI>
 __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const RowdotArgs a) {
@@ -133,7 +137,10 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
     const int upw = paired ? kH : kR;                             // output units per wave
     const int n_units = (EPI == EPI_QKV && paired) ? sg.N / 2 : sg.N;
     const int ksplit = a.ksplit;
-    const int grp = wave / ksplit, ks = wave - grp * ksplit;
+    constexpr int NS = EPI == EPI_SWIGLU ? 2 : 1;                 // wave sets per unit group
+    const int grp = wave / (NS * ksplit);
+    const int half = (wave / ksplit) % NS;                        // SwiGLU: 0 = gate, 1 = up
+    const int ks = wave % ksplit;
     const int unit0 = (bid - sg.blk_begin) * sg.units_per_blk + grp * upw;
     const int halfD = a.D >> 1;
 
@@ -144,16 +151,12 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
     int aoff[kR];
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
-        int u, n, mat = 0;
+        int u, n;
+        const int mat = EPI == EPI_SWIGLU ? half : 0;
         if (paired) {
             u = unit0 + r % kH;
-            if (EPI == EPI_SWIGLU) {
-                mat = r / kH;
-                n = u;
-            } else {
-                const int h = u / halfD, i = u - h * halfD;
-                n = h * a.D + i + (r / kH) * halfD;
-            }
+            const int h = u / halfD, i = u - h * halfD;
+            n = h * a.D + i + (r / kH) * halfD;
         } else {
             u = unit0 + r;
             n = u;
@@ -188,11 +191,10 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
     // One pass per U steps: every W and activation load of the pass is issued before the first
     // product (predicated, branch-free), so a wave waits for HBM once per pass.
     constexpr int U = BMAX <= 2 ? 4 : (BMAX <= 8 ? 2 : 1);
-    constexpr int NA = EPI == EPI_SWIGLU ? 2 : 1;  // distinct activation vectors (gate, up)
-    const int ka0 = EPI == EPI_SWIGLU ? sg.K : k_hi, ka1 = EPI == EPI_SWIGLU ? sg.K2 : k_hi;
+    const int ka = EPI == EPI_SWIGLU ? (half ? sg.K2 : sg.K) : k_hi;  // activation length
     for (int kb = k_lo; kb < k_hi; kb += 64 * E * U) {
         u32x4 wv[U][kR];
-        u32x4 av[U][BMAX][NA];
+        u32x4 av[U][BMAX];
         u32x4 nw[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -209,12 +211,8 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
             nw[u] = (norm_w && in) ? ldg16(a.norm_w + k) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int b = 0; b < BMAX; ++b) {
-#pragma unroll
-                for (int x = 0; x < NA; ++x) {
-                    const int off = x ? aoff[kH] : aoff[0];
-                    const bool ok = b < M && in && k < (x ? ka1 : ka0);
-                    av[u][b][x] = ok ? ldg16(act + b * lda_b + (int64_t)(off + k) * sizeof(T)) : u32x4{0u, 0u, 0u, 0u};
-                }
+                const bool ok = b < M && in && k < ka;
+                av[u][b] = ok ? ldg16(act + b * lda_b + (int64_t)(aoff[0] + k) * sizeof(T)) : u32x4{0u, 0u, 0u, 0u};
             }
         }
 #pragma unroll
@@ -222,20 +220,15 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
 #pragma unroll
             for (int b = 0; b < BMAX; ++b) {
                 if (b >= M) continue;
-                if constexpr (EPI == EPI_SWIGLU) {
-#pragma unroll
-                    for (int r = 0; r < kR; ++r) acc[r][b] = vdot(wv[u][r], av[u][b][r / kH], acc[r][b], T());
-                } else {
-                    u32x4 x = av[u][b][0];
-                    if constexpr (EPI == EPI_Z) {
-                        if (norm) {
-                            ss[b] += vsq(x, T());
-                            if (norm_w) x = vmulw(x, nw[u]);
-                        }
+                u32x4 x = av[u][b];
+                if constexpr (EPI == EPI_Z) {
+                    if (norm) {
+                        ss[b] += vsq(x, T());
+                        if (norm_w) x = vmulw(x, nw[u]);
                     }
-#pragma unroll
-                    for (int r = 0; r < kR; ++r) acc[r][b] = vdot(wv[u][r], x, acc[r][b], T());
                 }
+#pragma unroll
+                for (int r = 0; r < kR; ++r) acc[r][b] = vdot(wv[u][r], x, acc[r][b], T());
             }
         }
     }
@@ -262,14 +255,17 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
         if (a.adv_seqlens != nullptr && bid == 0 && tid < a.adv_B) a.adv_seqlens[tid] += a.adv_n;
     }
 
-    auto val = [&](int g, int r, int b) -> float {
+    // value r (row or statistic) of unit group g, wave set h, activation row b: the sum over the
+    // ksplit waves of that set and their 4 DPP rows
+    auto val = [&](int g, int h, int r, int b) -> float {
         float s = 0.f;
-        for (int w = g * ksplit; w < (g + 1) * ksplit; ++w)
+        const int w0 = (g * NS + h) * ksplit;
+        for (int w = w0; w < w0 + ksplit; ++w)
             s += red[w][0][r * BMAX + b] + red[w][1][r * BMAX + b] + red[w][2][r * BMAX + b] + red[w][3][r * BMAX + b];
         return s;
     };
 
-    const int ngroups = a.waves / ksplit;
+    const int ngroups = a.waves / (NS * ksplit);
     const int total = ngroups * upw * M;
     for (int idx = tid; idx < total; idx += 64 * a.waves) {
         const int g = idx / (upw * M);
@@ -279,34 +275,34 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
         const int u = (bid - sg.blk_begin) * sg.units_per_blk + g * upw + j;
         if (u >= n_units) continue;
         if constexpr (EPI == EPI_Z) {
-            float v = val(g, j, m);
+            float v = val(g, 0, j, m);
             if (a.norm) {
-                const float sq = val(g, kR, m);
+                const float sq = val(g, 0, kR, m);
                 v *= 1.0f / sqrtf(sq / (float)a.norm_K + a.norm_eps);
             }
             store_t<T>(sg.out, (int64_t)m * sg.ldo + u, v);
         } else if constexpr (EPI == EPI_LINEAR) {
-            float v = val(g, j, m);
+            float v = val(g, 0, j, m);
             if (a.bias) v += load_t<T>(a.bias, u);
             if (a.residual) v += load_t<T>(a.residual, (int64_t)m * a.ldr + u);
             store_t<T>(sg.out, (int64_t)m * sg.ldo + u, v);
         } else if constexpr (EPI == EPI_GELU) {
-            store_t<T>(sg.out, (int64_t)m * sg.ldo + u, gelu_f(val(g, j, m)));
+            store_t<T>(sg.out, (int64_t)m * sg.ldo + u, gelu_f(val(g, 0, j, m)));
         } else if constexpr (EPI == EPI_SWIGLU) {
-            const float gv = val(g, j, m), uv = val(g, j + kH, m);
+            const float gv = val(g, 0, j, m), uv = val(g, 1, j, m);
             store_t<T>(sg.out, (int64_t)m * sg.ldo + u, silu_f(gv) * uv);
         } else if constexpr (EPI == EPI_QKV) {
             const int b = m / a.S, s = m - b * a.S;
             const int64_t p = (int64_t)a.seqlens[b] + s;
             const bool in_cache = p >= 0 && p < a.L_max;
             if (sg.kind == SEG_V) {
-                const bf16_t bits = f2bf(val(g, j, m));
+                const bf16_t bits = f2bf(val(g, 0, j, m));
                 const int hd = a.Hkv * a.D;
                 if (in_cache) a.v_cache[((int64_t)b * a.L_max + p) * hd + u] = bits;
                 else set_dev_error(a.err, FSVD_DEVERR_KV_OVERFLOW);
                 if (a.v_out) a.v_out[(int64_t)m * hd + u] = bits;
             } else {
-                const float x1 = val(g, j, m), x2 = val(g, j + kH, m);
+                const float x1 = val(g, 0, j, m), x2 = val(g, 0, j + kH, m);
                 const int h = u / halfD, i = u - h * halfD;
                 const int n1 = h * a.D + i, n2 = n1 + halfD;
                 float y1 = x1, y2 = x2;
@@ -364,21 +360,22 @@ int rowdot_plan(RowdotArgs& a, int epi) {
         const bool paired = seg_paired(epi, s.kind);
         kmax = std::max(kmax, std::max(s.K, epi == EPI_SWIGLU ? s.K2 : 0));
         const int u = (epi == EPI_QKV && paired) ? s.N / 2 : s.N;
-        units += paired ? (u + kH - 1) / kH : (u + kR - 1) / kR;  // row groups
+        units += wave_sets(epi) * (paired ? (u + kH - 1) / kH : (u + kR - 1) / kR);  // waves without split
     }
     int ksplit = 1;
     while (ksplit < 8 && (kmax + ksplit - 1) / ksplit > 1024 && kmax / (ksplit * 2) >= 256) ksplit *= 2;
     while (ksplit < 8 && (int64_t)units * ksplit < 2048 && kmax / (ksplit * 2) >= 256) ksplit *= 2;
     if (a.M > 16) ksplit = std::min(ksplit, 4);  // the 32-row variant runs 4-wave workgroups
+    if (epi == EPI_SWIGLU) ksplit = std::min(ksplit, a.M > 16 ? 2 : 4);  // two wave sets per group
     a.ksplit = ksplit;
-    a.waves = ksplit > 4 ? 8 : 4;
+    a.waves = wave_sets(epi) * ksplit > 4 ? 8 : 4;
     int blk = 0;
     for (int i = 0; i < a.nseg; ++i) {
         RowdotSeg& s = a.seg[i];
         const bool paired = seg_paired(epi, s.kind);
         const int upw = paired ? kH : kR;
         const int n_units = (epi == EPI_QKV && paired) ? s.N / 2 : s.N;
-        s.units_per_blk = (a.waves / ksplit) * upw;
+        s.units_per_blk = (a.waves / (wave_sets(epi) * ksplit)) * upw;
         s.blk_begin = blk;
         blk += (n_units + s.units_per_blk - 1) / s.units_per_blk;
     }
