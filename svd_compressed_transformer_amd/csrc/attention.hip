@@ -82,21 +82,26 @@ __global__ __launch_bounds__(256) void attn_decode_split(const AttnArgs a) {
     const bf16_t* kbase = a.kc + ((int64_t)b * a.L_max * a.Hkv + kvh) * D + li * EPL;
     const bf16_t* vbase = a.vc + ((int64_t)b * a.L_max * a.Hkv + kvh) * D + li * EPL;
 
-    constexpr int NP = 2;  // positions per lane group per iteration
-    for (int64_t jb = j0 + lg; jb < j1; jb += 16 * NP) {
-        KV<EPL> kv[NP], vv[NP];
-        bool ok[NP];
+    // NP positions per lane group per iteration; the K/V vectors of the next iteration are loaded
+    // before the current ones are used, so every wave keeps two iterations of loads in flight
+    constexpr int NP = 2;
+    KV<EPL> kv[NP], vv[NP];
+    auto load = [&](int64_t jb, KV<EPL> (&kk)[NP], KV<EPL> (&vk)[NP]) {
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int64_t j = jb + 16 * p;
-            ok[p] = j < j1;
-            const int64_t jj = ok[p] ? j : jb;
-            kv[p] = ld_kv<EPL>(kbase + jj * rowstride);
-            vv[p] = ld_kv<EPL>(vbase + jj * rowstride);
+            const int64_t jj = j < j1 ? j : j0;  // rows past the partition re-read its first row
+            kk[p] = ld_kv<EPL>(kbase + jj * rowstride);
+            vk[p] = ld_kv<EPL>(vbase + jj * rowstride);
         }
+    };
+    if (j0 + lg < j1) load(j0 + lg, kv, vv);
+    for (int64_t jb = j0 + lg; jb < j1; jb += 16 * NP) {
+        KV<EPL> kn[NP], vn[NP];
+        if (jb + 16 * NP < j1) load(jb + 16 * NP, kn, vn);
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            if (!ok[p]) continue;  // uniform over the lane group (one DPP row)
+            if (jb + 16 * p >= j1) continue;  // uniform over the lane group (one DPP row)
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 float d = 0.f;
@@ -114,6 +119,11 @@ __global__ __launch_bounds__(256) void attn_decode_split(const AttnArgs a) {
                     o[g][2 * i + 1] = o[g][2 * i + 1] * alpha + pr * bf_hi(vv[p].w[i]);
                 }
             }
+        }
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            kv[p] = kn[p];
+            vv[p] = vn[p];
         }
     }
 
@@ -152,36 +162,42 @@ __global__ __launch_bounds__(256) void attn_decode_split(const AttnArgs a) {
     }
 }
 
-// merge partitions: one workgroup per (b, h).  The first wave reads every partition's
-// (max, sum) at once and forms the log-sum-exp weights; then each thread owns one head element
-// and sums the weighted partial outputs (all loads independent, so one L2 round trip).
+// merge partitions: one workgroup per (b, h), one thread per head element.  Every thread loads
+// its element of all partitions together with the partitions' (max, sum) statistics, so the
+// merge costs a single round trip to L2; partitions are taken 16 at a time.
 __global__ __launch_bounds__(128) void attn_decode_combine(const AttnArgs a) {
     const int D = a.D, ns = a.nsplit;
     const int bh = blockIdx.x;
     const int t = threadIdx.x;
-    const float* part = a.part + (int64_t)bh * ns * (D + 2);
-    __shared__ float w[64];
-    __shared__ float inv_l;
-    if (t < 64) {
-        const bool ok = t < ns;
-        const float ms = ok ? part[t * (D + 2) + D] : kNegBig;
-        const float ls = ok ? part[t * (D + 2) + D + 1] : 0.f;
-        float M = row16_max(ms);
-        M = fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, M), 0)),
-                        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, M), 16))),
-                  fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, M), 32)),
-                        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, M), 48))));
-        const float ws = ok ? exp2f(ms - M) : 0.f;
-        w[t] = ws;
-        const float L = wave_sum(ws * ls);
-        if (t == 0) inv_l = 1.0f / L;
-    }
-    __syncthreads();
     if (t >= D) return;
-    float O = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < ns; ++s) O += w[s] * part[s * (D + 2) + t];
-    a.out[(int64_t)bh * D + t] = f2bf(O * inv_l);
+    const float* part = a.part + (int64_t)bh * ns * (D + 2);
+    constexpr int C = 16;
+    float M = kNegBig, L = 0.f, O = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += C) {
+        float ms[C], ls[C], os[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const bool ok = s0 + c < ns;
+            const float* row = part + (int64_t)(ok ? s0 + c : s0) * (D + 2);
+            ms[c] = ok ? row[D] : kNegBig;
+            ls[c] = row[D + 1];
+            os[c] = row[t];
+        }
+        float mc = M;
+#pragma unroll
+        for (int c = 0; c < C; ++c) mc = fmaxf(mc, ms[c]);
+        const float r = exp2f(M - mc);
+        L *= r;
+        O *= r;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const float w = exp2f(ms[c] - mc);  // 0 for the padding entries (max = -1e30)
+            L += w * ls[c];
+            O += w * os[c];
+        }
+        M = mc;
+    }
+    a.out[(int64_t)bh * D + t] = f2bf(O / L);
 }
 
 template <int EPL>
