@@ -3,12 +3,13 @@
 // At prefill the two phases of y = (x . U) . V are dense contractions with M = B*S in the
 // thousands (about M flop per factor byte, far above the MFMA ridge), so each phase runs as an
 // NT GEMM C[M, N] = A[M, K] . B[N, K]^T on the matrix cores with a fused epilogue:
-//   - tiles of BM x BN (256 or 128 x 256 or 128), BK = 64, four waves as 2 x 2, each wave a grid
-//     of 32 x 32 blocks computed with v_mfma_f32_32x32x16_bf16 (fp32 accumulation);
+//   - tiles of BM x BN (256 or 128 x 256 or 128), four waves as 2 x 2, each wave a grid of
+//     32 x 32 blocks computed with v_mfma_f32_32x32x16_bf16 (fp32 accumulation);
 //   - operands move global -> LDS directly (global_load_lds_dwordx4, no staging registers) through
-//     a 4-stage pipeline of BK = 32 slices, each lane choosing the global chunk whose XOR-swizzled
-//     LDS home is its slot, so the 32-row fragment reads of one MFMA hit distinct banks; M/N tails
-//     re-read the last row (never stored), the K tail is zeroed in LDS;
+//     a 2- or 3-stage pipeline of BK = 64 slices (one whole 128-byte line per row and stage, which
+//     the load path serves about 1.4x faster than half lines), each lane choosing the global chunk
+//     whose XOR-swizzled LDS home is its slot, so the fragment reads of one MFMA hit distinct
+//     banks; M/N tails re-read the last row (never stored), the K tail is zeroed in LDS;
 //   - tiles are handed out XCD by XCD (workgroup i runs on XCD i mod 8) so the WGs that share an
 //     XCD's L2 work on neighbouring M tiles of one N tile and reuse its B operand.
 // Epilogues: per-row scale (RMSNorm folded after the product), bias + residual, Q/K/V with
@@ -27,30 +28,44 @@ namespace {
 typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BK = 32;          // k per LDS stage: 4 chunks of 16 bytes per row
-constexpr int kStages = 4;      // LDS pipeline depth
 constexpr int kThreads = 256;   // 4 waves, arranged 2 x 2
+
+// Per tile shape: k per LDS stage (KB) and pipeline depth.  256 x 256 tiles stage BK = 32 slices
+// four deep (4 x 32 KiB); 128 x 256 and 256 x 128 tiles stage BK = 64 slices, one whole 128-byte
+// line per row (the load path serves whole lines about 1.4x faster than half lines), three deep
+// (3 x 48 KiB).  Measured on MI355X, the deeper pipeline matters more for the big tile.
+template <int BM, int BN>
+constexpr int kb_for() { return BM + BN > 384 ? 32 : 64; }
+template <int BM, int BN>
+constexpr int stages_for() { return kb_for<BM, BN>() == 32 ? 4 : 3; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// chunk c of row r of a stage buffer sits at chunk slot r * 4 + (c ^ ((r >> 2) & 3)): the 16 rows
-// read by one quarter-wave for an MFMA fragment then fall in 16 distinct 16-byte bank groups
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 4 + (chunk ^ ((row >> 2) & 3)); }
+// Swizzled home of chunk c (16 bytes) of row r in a stage buffer.  KB = 64: rows of 8 chunks
+// (128 bytes, half the 64 x 4-byte banks), slot r * 8 + (c ^ ((r >> 1) & 7)); KB = 32: rows of 4
+// chunks, slot r * 4 + (c ^ ((r >> 2) & 3)).  Either way the 16 rows read by one quarter-wave for
+// an MFMA fragment cover 16 distinct 16-byte bank groups.
+template <int KB>
+__device__ __forceinline__ int swz(int row, int chunk) {
+    if constexpr (KB == 64) return row * 8 + (chunk ^ ((row >> 1) & 7));
+    else return row * 4 + (chunk ^ ((row >> 2) & 3));
+}
 
-// Issue the direct global -> LDS loads of one operand tile (ROWS x BK) into stage buffer 'dst'.
+// Issue the direct global -> LDS loads of one operand tile (ROWS x KB) into stage buffer 'dst'.
 // A wave instruction writes 64 consecutive 16-byte slots; each lane picks the global chunk whose
 // swizzled home is its slot.  Rows past 'rows' re-read the last row (their products are never
 // stored); chunks past K are clamped inside the row and zeroed by zero_k_tail() before use.
-template <int ROWS>
+template <int ROWS, int KB>
 __device__ __forceinline__ void issue_tile(const bf16_t* base, int64_t ld, int row0, int rows, int k0, int K,
                                            u32x4* dst, int wave, int lane) {
-    constexpr int PER_WAVE = ROWS * 4 / 64 / 4;  // instructions per wave
+    constexpr int CPR = KB / 8;
+    constexpr int PER_WAVE = ROWS * CPR / kThreads;  // instructions per wave
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
         const int slot0 = (wave * PER_WAVE + i) * 64;
         const int slot = slot0 + lane;
-        const int r = slot >> 2, phys = slot & 3;
-        const int c = phys ^ ((r >> 2) & 3);
+        const int r = slot / CPR, phys = slot % CPR;
+        const int c = KB == 64 ? (phys ^ ((r >> 1) & 7)) : (phys ^ ((r >> 2) & 3));
         const int gr = min(row0 + r, rows - 1);
         const int gk = min(k0 + c * 8, K - 8);
         __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)gr * ld + gk), (lds_void*)(dst + slot0), 16, 0, 0);
@@ -58,16 +73,13 @@ __device__ __forceinline__ void issue_tile(const bf16_t* base, int64_t ld, int r
 }
 
 // zero the chunks of a stage whose k index is >= K (only the last k tile can have them)
-template <int ROWS>
+template <int ROWS, int KB>
 __device__ __forceinline__ void zero_k_tail(u32x4* dst, int k0, int K, int tid) {
-    for (int q = tid; q < ROWS * 4; q += kThreads) {
-        const int r = q >> 2, c = q & 3;
-        if (k0 + c * 8 >= K) dst[swz(r, c)] = u32x4{0u, 0u, 0u, 0u};
+    constexpr int CPR = KB / 8;
+    for (int q = tid; q < ROWS * CPR; q += kThreads) {
+        const int r = q / CPR, c = q % CPR;
+        if (k0 + c * 8 >= K) dst[swz<KB>(r, c)] = u32x4{0u, 0u, 0u, 0u};
     }
-}
-
-__device__ __forceinline__ bf16x8_v frag(const u32x4* lds, int row, int chunk) {
-    return __builtin_bit_cast(bf16x8_v, lds[swz(row, chunk)]);
 }
 
 // s_waitcnt on the vector-memory counter only: vmcnt in bits [3:0] and [15:14], expcnt (bits 6:4)
@@ -75,7 +87,8 @@ __device__ __forceinline__ bf16x8_v frag(const u32x4* lds, int row, int chunk) {
 #define FSVD_VMCNT(n) (0x0F70 | ((n) & 0xF) | ((((n) >> 4) & 3) << 14))
 __device__ __forceinline__ void wait_vm(int n) {
     // wait until at most n vector-memory operations of this wave are outstanding (n rounded down)
-    if (n >= 16) __builtin_amdgcn_s_waitcnt(FSVD_VMCNT(16));
+    if (n >= 24) __builtin_amdgcn_s_waitcnt(FSVD_VMCNT(24));
+    else if (n >= 16) __builtin_amdgcn_s_waitcnt(FSVD_VMCNT(16));
     else if (n >= 12) __builtin_amdgcn_s_waitcnt(FSVD_VMCNT(12));
     else if (n >= 8) __builtin_amdgcn_s_waitcnt(FSVD_VMCNT(8));
     else if (n >= 6) __builtin_amdgcn_s_waitcnt(FSVD_VMCNT(6));
@@ -92,31 +105,33 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Instruction order for one pipeline phase of NM MFMAs: the NR LDS reads and the NG global loads
-// issued in that phase are spread evenly between the MFMAs (reads first), so they issue in the
-// shadow of the matrix cores instead of in a burst that stalls them.
+// Instruction order for one pipeline step of NM MFMAs: one memory instruction after each of the
+// first MFMAs, the NR LDS reads (fragments of the next k step) first so they land well before
+// the step ends, then the NG global loads, then the remaining MFMAs.
 template <int NR, int NG, int NM, int Q = 0>
 __device__ __forceinline__ void sched_interleave() {
-    constexpr int NX = NG + NR;
-    constexpr int per = NX ? (NM + NX - 1) / NX : NM;  // MFMAs between two memory instructions
-    constexpr int left = NM - Q * per > 0 ? NM - Q * per : 0;
-    constexpr int m = left < per ? left : per;
+    constexpr int NX = NR + NG;
     if constexpr (Q < NX) {
-        if constexpr (m > 0) __builtin_amdgcn_sched_group_barrier(0x008, m, 0);
+        if constexpr (Q < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(Q < NR ? 0x100 : 0x020, 1, 0);
         sched_interleave<NR, NG, NM, Q + 1>();
-    } else if constexpr (left > 0) {
-        __builtin_amdgcn_sched_group_barrier(0x008, left, 0);
+    } else if constexpr (NM > NX) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NM - NX, 0);
     }
 }
 
 // C tile accumulation over k in [0, K): acc[i][j] += A[wm + 32 i + .., k] . B[wn + 32 j + .., k]
 template <int BM, int BN>
 struct Tile {
+    static constexpr int KB = kb_for<BM, BN>();          // k per stage
+    static constexpr int CPR = KB / 8;                   // 16-byte chunks per row and stage
+    static constexpr int S = stages_for<BM, BN>();       // LDS stages
     static constexpr int WM = BM / 2, WN = BN / 2;      // wave tile
     static constexpr int FI = WM / 32, FJ = WN / 32;    // 32x32 blocks per wave
-    static constexpr int STAGE = (BM + BN) * 4;         // 16-byte slots per stage
-    static constexpr int LOADS = (BM + BN) * 4 / 64 / 4;  // load instructions per wave per stage
+    static constexpr int STAGE = (BM + BN) * CPR;       // 16-byte slots per stage
+    static constexpr int LOADS = STAGE / kThreads;      // load instructions per wave per stage
+    static constexpr int KSUB = KB / 16;                // 16-wide MFMA k steps per stage
+    static constexpr size_t LDS_BYTES = (size_t)S * STAGE * 16;
     f32x16 acc[FI][FJ];
 
     __device__ __forceinline__ void zero() {
@@ -128,16 +143,16 @@ struct Tile {
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
     }
 
-    // fragments of one 16-wide k step (substep kk of a BK = 32 stage) for this wave
+    // fragments of k step kk (0 .. KSUB-1) of a stage for this wave
     __device__ __forceinline__ void read_frags(const u32x4* st, int kk, int wm, int wn, int lane, bf16x8_v (&af)[FI],
                                                bf16x8_v (&bf)[FJ]) {
         const u32x4* pa = st;
-        const u32x4* pb = st + BM * 4;
+        const u32x4* pb = st + BM * CPR;
         const int ch = kk * 2 + (lane >> 5);
 #pragma unroll
-        for (int i = 0; i < FI; ++i) af[i] = frag(pa, wm + i * 32 + (lane & 31), ch);
+        for (int i = 0; i < FI; ++i) af[i] = __builtin_bit_cast(bf16x8_v, pa[swz<KB>(wm + i * 32 + (lane & 31), ch)]);
 #pragma unroll
-        for (int j = 0; j < FJ; ++j) bf[j] = frag(pb, wn + j * 32 + (lane & 31), ch);
+        for (int j = 0; j < FJ; ++j) bf[j] = __builtin_bit_cast(bf16x8_v, pb[swz<KB>(wn + j * 32 + (lane & 31), ch)]);
     }
 
     __device__ __forceinline__ void mfmas(const bf16x8_v (&af)[FI], const bf16x8_v (&bf)[FJ]) {
@@ -148,76 +163,81 @@ struct Tile {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
 
-    // Software pipeline over k tiles, two 16-wide substeps per tile.  Global -> LDS loads run
-    // three tiles ahead; within a tile, the fragments of the next substep are read from LDS while
-    // the MFMAs of the current one run, so the matrix cores wait neither for LDS nor at the single
-    // barrier per tile, which sits between the two substeps:
-    //   [loads of tile kt+3] [reads F1(kt)] [MFMA F0(kt)] wait tile kt+1, barrier
-    //   [reads F0(kt+1)] [MFMA F1(kt)]
+    // Software pipeline over k tiles (S LDS stages, KSUB MFMA k steps per tile).  Global -> LDS
+    // loads run S - 1 tiles ahead; within a tile the fragments of the next k step are read from LDS
+    // while the MFMAs of the current one run, so the matrix cores wait neither for LDS nor at the
+    // single barrier per tile, which sits before the last k step (KSUB = 4 shown):
+    //   [reads F1, loads A of tile kt+S-1, MFMA F0] [reads F2, loads B, MFMA F1] [reads F3, MFMA F2]
+    //   wait for tile kt+1, barrier, [reads F0 of tile kt+1, MFMA F3]
     // The barrier makes tile kt+1 visible and retires every wave's reads of tile kt, whose stage
-    // the next iteration's loads (tile kt+4) overwrite.
+    // the next iteration's loads (tile kt+S) overwrite.
+    template <bool ISSUE>
+    __device__ __forceinline__ void step(int kt, int nk, const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ldb,
+                                         int m0, int n0, int M, int N, int K, u32x4* smem, int tid, int wm, int wn,
+                                         bf16x8_v (&af)[2][FI], bf16x8_v (&bf)[2][FJ]) {
+        const int lane = tid & 63, wave = tid >> 6;
+        constexpr int LA = BM * CPR / kThreads, LB = BN * CPR / kThreads;  // loads per operand
+        constexpr int KB_B = KSUB > 2 ? 1 : 0;                             // k step issuing the B loads
+        const u32x4* st = smem + (kt % S) * STAGE;
+        u32x4* dst = smem + ((kt + S - 1) % S) * STAGE;
+#pragma unroll
+        for (int kk = 0; kk + 1 < KSUB; ++kk) {
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(st, kk + 1, wm, wn, lane, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
+            if constexpr (ISSUE) {
+                if (kk == 0) issue_tile<BM, KB>(A, lda, m0, M, (kt + S - 1) * KB, K, dst, wave, lane);
+                if (kk == KB_B) issue_tile<BN, KB>(B, ldb, n0, N, (kt + S - 1) * KB, K, dst + BM * CPR, wave, lane);
+            }
+            mfmas(af[kk & 1], bf[kk & 1]);
+            constexpr int ng0 = ISSUE ? (KB_B == 0 ? LA + LB : LA) : 0;
+            constexpr int ng1 = ISSUE ? LB : 0;
+            if (kk == 0) sched_interleave<FI + FJ, ng0, FI * FJ>();
+            else if (kk == KB_B) sched_interleave<FI + FJ, ng1, FI * FJ>();
+            else sched_interleave<FI + FJ, 0, FI * FJ>();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + 1 < nk) {
+            // tiles issued so far: 0 .. min(kt + S - 1, nk - 1); tile kt + 1 must have landed
+            wait_vm((min(kt + S - 1, nk - 1) - (kt + 1)) * LOADS);
+            if (kt + 1 == nk - 1 && K % KB) {
+                lds_barrier();
+                u32x4* last = smem + ((kt + 1) % S) * STAGE;
+                zero_k_tail<BM, KB>(last, (kt + 1) * KB, K, tid);
+                zero_k_tail<BN, KB>(last + BM * CPR, (kt + 1) * KB, K, tid);
+            }
+            lds_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(smem + ((kt + 1) % S) * STAGE, 0, wm, wn, lane, af[0], bf[0]);
+        }
+        mfmas(af[(KSUB - 1) & 1], bf[(KSUB - 1) & 1]);
+        sched_interleave<FI + FJ, 0, FI * FJ>();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
     __device__ __forceinline__ void run(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ldb, int m0, int n0,
                                         int M, int N, int K, u32x4* smem, int tid) {
         const int lane = tid & 63, wave = tid >> 6;
         const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
-        const int nk = (K + BK - 1) / BK;
-        auto issue = [&](int t) {
-            u32x4* st = smem + (t % kStages) * STAGE;
-            issue_tile<BM>(A, lda, m0, M, t * BK, K, st, wave, lane);
-            issue_tile<BN>(B, ldb, n0, N, t * BK, K, st + BM * 4, wave, lane);
-        };
-        // the last tile's chunks past K are zeroed once it has landed (all waves), before any read
-        auto k_tail = [&](int t) {
-            if (t == nk - 1 && K % BK) {
-                lds_barrier();
-                u32x4* st = smem + (t % kStages) * STAGE;
-                zero_k_tail<BM>(st, t * BK, K, tid);
-                zero_k_tail<BN>(st + BM * 4, t * BK, K, tid);
-            }
-        };
-        bf16x8_v a0[FI], b0[FJ], a1[FI], b1[FJ];
-        // prologue: tiles 0 .. 2 in flight, tile 0 landed, F0(0) read
-        const int pro = min(nk, kStages - 1);
-        for (int t = 0; t < pro; ++t) issue(t);
+        const int nk = (K + KB - 1) / KB;
+        bf16x8_v af[2][FI], bf[2][FJ];
+        // prologue: tiles 0 .. S-2 in flight, tile 0 landed (and K-tail zeroed), F0(0) read
+        const int pro = min(nk, S - 1);
+        for (int t = 0; t < pro; ++t) {
+            u32x4* dst = smem + (t % S) * STAGE;
+            issue_tile<BM, KB>(A, lda, m0, M, t * KB, K, dst, wave, lane);
+            issue_tile<BN, KB>(B, ldb, n0, N, t * KB, K, dst + BM * CPR, wave, lane);
+        }
         wait_vm((pro - 1) * LOADS);
-        k_tail(0);
-        lds_barrier();
-        read_frags(smem, 0, wm, wn, lane, a0, b0);
-
-        // steady state: every iteration issues tile kt + 3, so tiles kt+2 and kt+3 may still be
-        // in flight when tile kt+1 must have landed
-        int kt = 0;
-        for (; kt + kStages - 1 < nk; ++kt) {
-            // phase A: loads of tile kt+3 and reads of F1(kt) interleaved with the MFMAs of F0(kt)
-            __builtin_amdgcn_sched_barrier(0);
-            const u32x4* st = smem + (kt % kStages) * STAGE;
-            read_frags(st, 1, wm, wn, lane, a1, b1);
-            issue(kt + kStages - 1);
-            mfmas(a0, b0);
-            sched_interleave<FI + FJ, 2 * LOADS, FI * FJ>();
-            __builtin_amdgcn_sched_barrier(0);
-            wait_vm((kStages - 2) * LOADS);
+        if (nk == 1 && K % KB) {
             lds_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-            // phase B: reads of F0(kt+1) interleaved with the MFMAs of F1(kt)
-            read_frags(smem + ((kt + 1) % kStages) * STAGE, 0, wm, wn, lane, a0, b0);
-            mfmas(a1, b1);
-            sched_interleave<FI + FJ, 0, FI * FJ>();
-            __builtin_amdgcn_sched_barrier(0);
+            zero_k_tail<BM, KB>(smem, 0, K, tid);
+            zero_k_tail<BN, KB>(smem + BM * CPR, 0, K, tid);
         }
-        // drain: no more loads to issue
-        for (; kt < nk; ++kt) {
-            const u32x4* st = smem + (kt % kStages) * STAGE;
-            read_frags(st, 1, wm, wn, lane, a1, b1);
-            mfmas(a0, b0);
-            if (kt + 1 < nk) {
-                wait_vm((nk - 2 - kt) * LOADS);
-                k_tail(kt + 1);
-                lds_barrier();
-                read_frags(smem + ((kt + 1) % kStages) * STAGE, 0, wm, wn, lane, a0, b0);
-            }
-            mfmas(a1, b1);
-        }
+        lds_barrier();
+        read_frags(smem, 0, wm, wn, lane, af[0], bf[0]);
+        int kt = 0;
+        for (; kt + S - 1 < nk; ++kt) step<true>(kt, nk, A, lda, B, ldb, m0, n0, M, N, K, smem, tid, wm, wn, af, bf);
+        for (; kt < nk; ++kt) step<false>(kt, nk, A, lda, B, ldb, m0, n0, M, N, K, smem, tid, wm, wn, af, bf);
         __syncthreads();  // the caller may reuse the stage buffers
     }
 };
@@ -331,27 +351,88 @@ void gemm_kernel(const GemmArgs g) {
         return;
     }
 
+    // Row epilogue through LDS: each wave stages one 32-row block of its fp32 tile at a time
+    // (the MFMA layout gives a lane one column of 16 rows), then reads it back by rows so that a
+    // lane owns 8 consecutive columns: the per-row scale, bias, residual and activation are
+    // applied there and the result leaves as one 16-byte store (bias and residual arrive as
+    // 16-byte loads), instead of 2-byte stores scattered over the tile.
+    constexpr int SROW = T::WN + 8;        // staged row stride in floats (rows 4 apart: 32 banks apart)
+    constexpr int LPR = T::WN / 8;         // lanes per row in the row layout
+    constexpr int RP = 64 / LPR;           // rows per pass
+    float* stg = reinterpret_cast<float*>(smem) + wave * 32 * SROW;
+    const int rl = lane / LPR, c8 = (lane % LPR) * 8;
 #pragma unroll
     for (int i = 0; i < T::FI; ++i) {
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int row = wm + i * 32 + (e >> 2) * 8 + rsub + (e & 3);
-            if (row >= g.M) continue;
-            const float rs = g.rstd ? g.rstd[row] : 1.0f;
+            const int r = (e >> 2) * 8 + rsub + (e & 3);
 #pragma unroll
             for (int j = 0; j < T::FJ; ++j) {
-                const int col = wn + j * 32 + col_in;
-                if (col >= g.N) continue;
-                float y = t.acc[i][j][e] * rs;
-                if constexpr (EPI == GEPI_LINEAR) {
-                    if (g.bias) y += bf2f(g.bias[col]);
-                    if (g.residual) y += bf2f(g.residual[(int64_t)row * g.ldr + col]);
-                } else if constexpr (EPI == GEPI_SWIGLU) {
-                    y = silu_f(y) * t2.acc[i][j][e];
-                } else if constexpr (EPI == GEPI_GELU) {
-                    y = gelu_f(y);
+                float v = t.acc[i][j][e];
+                if constexpr (EPI == GEPI_SWIGLU) {
+                    const int row = wm + i * 32 + r;
+                    const float rs = (g.rstd && row < g.M) ? g.rstd[row] : 1.0f;
+                    v = silu_f(v * rs) * t2.acc[i][j][e];
                 }
-                g.C[(int64_t)row * g.ldc + col] = f2bf(y);
+                stg[r * SROW + j * 32 + col_in] = v;
+            }
+        }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int pass = 0; pass < 32 / RP; ++pass) {
+            const int r = pass * RP + rl;
+            const int row = wm + i * 32 + r;
+            const int col = wn + c8;
+            if (row >= g.M || col >= g.N) continue;
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(stg + r * SROW + c8);
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(stg + r * SROW + c8 + 4);
+            float y[8] = {__uint_as_float(lo.x), __uint_as_float(lo.y), __uint_as_float(lo.z), __uint_as_float(lo.w),
+                          __uint_as_float(hi.x), __uint_as_float(hi.y), __uint_as_float(hi.z), __uint_as_float(hi.w)};
+            const bool full = col + 8 <= g.N;
+            if constexpr (EPI != GEPI_SWIGLU) {
+                const float rs = g.rstd ? g.rstd[row] : 1.0f;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) y[q] *= rs;
+            }
+            if constexpr (EPI == GEPI_LINEAR) {
+                if (g.bias) {
+                    if (full) {
+                        const u32x4 bv = *reinterpret_cast<const u32x4*>(g.bias + col);
+                        const uint32_t w[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            y[2 * q] += bf_lo(w[q]);
+                            y[2 * q + 1] += bf_hi(w[q]);
+                        }
+                    } else {
+                        for (int q = 0; q < 8 && col + q < g.N; ++q) y[q] += bf2f(g.bias[col + q]);
+                    }
+                }
+                if (g.residual) {
+                    const bf16_t* rp = g.residual + (int64_t)row * g.ldr + col;
+                    if (full) {
+                        const u32x4 rv = *reinterpret_cast<const u32x4*>(rp);
+                        const uint32_t w[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            y[2 * q] += bf_lo(w[q]);
+                            y[2 * q + 1] += bf_hi(w[q]);
+                        }
+                    } else {
+                        for (int q = 0; q < 8 && col + q < g.N; ++q) y[q] += bf2f(rp[q]);
+                    }
+                }
+            } else if constexpr (EPI == GEPI_GELU) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) y[q] = gelu_f(y[q]);
+            }
+            bf16_t* cp = g.C + (int64_t)row * g.ldc + col;
+            if (full) {
+                *reinterpret_cast<u32x4*>(cp) =
+                    u32x4{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]), pack_bf2(y[4], y[5]), pack_bf2(y[6], y[7])};
+            } else {
+                for (int q = 0; q < 8 && col + q < g.N; ++q) cp[q] = f2bf(y[q]);
             }
         }
     }
@@ -360,7 +441,7 @@ void gemm_kernel(const GemmArgs g) {
 template <int BM, int BN, int EPI>
 fsvd_status_t launch_t(const GemmArgs& g, hipStream_t st) {
     const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-    const size_t lds = (size_t)kStages * (BM + BN) * BK * 2;
+    const size_t lds = Tile<BM, BN>::LDS_BYTES;
     static bool attr_set = false;
     if (!attr_set) {
         (void)hipFuncSetAttribute((const void*)gemm_kernel<BM, BN, EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
