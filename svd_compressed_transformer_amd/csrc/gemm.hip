@@ -289,106 +289,125 @@ void gemm_kernel(const GemmArgs g) {
     const int wm = m0 + (wave >> 1) * T::WM, wn = n0 + (wave & 1) * T::WN;
     const int col_in = lane & 31, rsub = (lane >> 5) * 4;
 
-    if constexpr (EPI == GEPI_QKV) {
-        // Pairs (c, c + D/2) of a head: the wave's column range is 128-aligned and holds whole
-        // heads, so the partner of block j is block j + D/64 in the same lane.
-        const int halfD = g.D >> 1, pb = halfD / 32;
-        const bool rope = g.seg != 2 && g.rope_theta > 0.f;
-        double rev[T::FJ];  // revolutions per position for the pair index of block j
+    // Staging buffer of the row epilogues: each wave stages one 32-row block of its fp32 tile at a
+    // time (the MFMA layout gives a lane one column of 16 rows) and reads it back by rows.
+    constexpr int SROW = T::WN + 8;        // staged row stride in floats (rows 4 apart: 32 banks apart)
+    float* stg = reinterpret_cast<float*>(smem) + wave * 32 * SROW;
+    // block i is selected with constant indices only (a runtime index into the accumulators
+    // would move them to scratch memory when the caller's loop over i is not unrolled)
+    auto stage = [&](int i) {
+        asm volatile("" ::: "memory");
 #pragma unroll
-        for (int j = 0; j < T::FJ; ++j) {
-            const int ip = ((wn + j * 32 + col_in) % g.D) % halfD;
-            rev[j] = exp2(-2.0 * (double)ip / (double)g.D * log2((double)g.rope_theta)) *
-                     0.15915494309189533576888376337251;  // 1 / (2 pi)
-        }
-#pragma unroll
-        for (int i = 0; i < T::FI; ++i) {
+        for (int ii = 0; ii < T::FI; ++ii) {
+            if (ii != i) continue;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int row = wm + i * 32 + (e >> 2) * 8 + rsub + (e & 3);
-                if (row >= g.M) continue;
-                const int b = row / g.S, s = row - b * g.S;
-                const int64_t p = (int64_t)g.seqlens[b] + s;
-                const bool in_cache = p >= 0 && p < g.L_max;
-                bf16_t* dst = g.seg == 0 ? g.q_out : (g.seg == 1 ? g.k_cache : g.v_cache);
-                bf16_t* dbg = g.seg == 1 ? g.k_out : (g.seg == 2 ? g.v_out : nullptr);
-                const int64_t drow = g.seg == 0 ? (int64_t)row * g.N : ((int64_t)b * g.L_max + p) * g.N;
-                const bool write = g.seg == 0 || in_cache;
-                if (!write) set_dev_error(g.err, FSVD_DEVERR_KV_OVERFLOW);
+                const int r = (e >> 2) * 8 + rsub + (e & 3);
 #pragma unroll
                 for (int j = 0; j < T::FJ; ++j) {
-                    const int col = wn + j * 32 + col_in;
-                    if (col >= g.N) continue;
-                    if (rope) {
-                        if ((j / pb) & 1) continue;  // second half: written with its partner
-                        const double tr = (double)p * rev[j];
+                    float v = t.acc[ii][j][e];
+                    if constexpr (EPI == GEPI_SWIGLU) {
+                        const int row = wm + ii * 32 + r;
+                        const float rs = (g.rstd && row < g.M) ? g.rstd[row] : 1.0f;
+                        v = silu_f(v * rs) * t2.acc[ii][j][e];
+                    }
+                    stg[r * SROW + j * 32 + col_in] = v;
+                }
+            }
+        }
+        asm volatile("" ::: "memory");
+    };
+    auto ld8 = [&](int r, int c, float (&y)[8]) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(stg + r * SROW + c);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(stg + r * SROW + c + 4);
+        y[0] = __uint_as_float(lo.x); y[1] = __uint_as_float(lo.y); y[2] = __uint_as_float(lo.z); y[3] = __uint_as_float(lo.w);
+        y[4] = __uint_as_float(hi.x); y[5] = __uint_as_float(hi.y); y[6] = __uint_as_float(hi.z); y[7] = __uint_as_float(hi.w);
+    };
+    auto pack8 = [](const float (&y)[8]) {
+        return u32x4{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]), pack_bf2(y[4], y[5]), pack_bf2(y[6], y[7])};
+    };
+
+    if constexpr (EPI == GEPI_QKV) {
+        // Row layout by RoPE pairs: a wave tile row holds whole heads (its 128 columns are
+        // 128-aligned), i.e. 64 pairs (c, c + D/2); a lane owns 8 consecutive pairs of a row,
+        // rotates them (sin/cos once per pair) and writes the two 16-byte halves, to the Q
+        // output or to the cache row of the token's position (and the optional K/V copies).
+        constexpr int LPR = T::WN / 16;    // lanes per row
+        constexpr int RP = 64 / LPR;       // rows per pass
+        const int halfD = g.D >> 1;
+        const bool rope = g.seg != 2 && g.rope_theta > 0.f;
+        const int pr0 = (lane % LPR) * 8;             // first pair slot of the lane in the row
+        const int h = pr0 / halfD, i0 = pr0 % halfD;  // head within the wave tile, pair index
+        const int c1 = h * g.D + i0, c2 = c1 + halfD;  // staged columns of the two halves
+        // revolutions per position of each pair index, computed once per workgroup into LDS past
+        // the staging buffers (after the k loop, so nothing of it is live across that loop)
+        double* rev = reinterpret_cast<double*>(reinterpret_cast<float*>(smem) + 4 * 32 * SROW);
+        if (tid < halfD)
+            rev[tid] = rope ? exp2(-2.0 * (double)tid / (double)g.D * log2((double)g.rope_theta)) *
+                                  0.15915494309189533576888376337251  // 1 / (2 pi)
+                            : 0.0;
+        __syncthreads();
+        bf16_t* dst = g.seg == 0 ? g.q_out : (g.seg == 1 ? g.k_cache : g.v_cache);
+        bf16_t* dbg = g.seg == 1 ? g.k_out : (g.seg == 2 ? g.v_out : nullptr);
+#pragma unroll
+        for (int i = 0; i < T::FI; ++i) {
+            stage(i);
+#pragma unroll
+            for (int pass = 0; pass < 32 / RP; ++pass) {
+                const int r = pass * RP + lane / LPR;
+                const int row = wm + i * 32 + r;
+                if (row >= g.M || wn + c2 >= g.N) continue;
+                const int b = row / g.S, s = row - b * g.S;
+                const int64_t p = (int64_t)g.seqlens[b] + s;
+                const bool write = g.seg == 0 || (p >= 0 && p < g.L_max);
+                if (!write) set_dev_error(g.err, FSVD_DEVERR_KV_OVERFLOW);
+                float x1[8], x2[8];
+                ld8(r, c1, x1);
+                ld8(r, c2, x2);
+                if (rope) {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const double tr = (double)p * rev[i0 + q];
                         const float ang = (float)((tr - floor(tr)) * 6.283185307179586476925286766559);
                         float c, sn;
                         sincosf(ang, &sn, &c);
-                        // partner block j + pb, selected with constant indices only
-                        const float x1 = t.acc[i][j][e];
-                        float x2 = 0.f;
-#pragma unroll
-                        for (int jj = 0; jj < T::FJ; ++jj)
-                            if (jj == j + pb) x2 = t.acc[i][jj][e];
-                        const bf16_t v1 = f2bf(x1 * c - x2 * sn), v2 = f2bf(x2 * c + x1 * sn);
-                        if (write) {
-                            dst[drow + col] = v1;
-                            dst[drow + col + halfD] = v2;
-                        }
-                        if (dbg) {
-                            dbg[(int64_t)row * g.N + col] = v1;
-                            dbg[(int64_t)row * g.N + col + halfD] = v2;
-                        }
-                    } else {
-                        const bf16_t v = f2bf(t.acc[i][j][e]);
-                        if (write) dst[drow + col] = v;
-                        if (dbg) dbg[(int64_t)row * g.N + col] = v;
+                        const float a = x1[q], bb = x2[q];
+                        x1[q] = a * c - bb * sn;
+                        x2[q] = bb * c + a * sn;
                     }
+                }
+                const u32x4 v1 = pack8(x1), v2 = pack8(x2);
+                const int64_t drow = g.seg == 0 ? (int64_t)row * g.N : ((int64_t)b * g.L_max + p) * g.N;
+                if (write) {
+                    *reinterpret_cast<u32x4*>(dst + drow + wn + c1) = v1;
+                    *reinterpret_cast<u32x4*>(dst + drow + wn + c2) = v2;
+                }
+                if (dbg) {
+                    *reinterpret_cast<u32x4*>(dbg + (int64_t)row * g.N + wn + c1) = v1;
+                    *reinterpret_cast<u32x4*>(dbg + (int64_t)row * g.N + wn + c2) = v2;
                 }
             }
         }
         return;
     }
 
-    // Row epilogue through LDS: each wave stages one 32-row block of its fp32 tile at a time
-    // (the MFMA layout gives a lane one column of 16 rows), then reads it back by rows so that a
-    // lane owns 8 consecutive columns: the per-row scale, bias, residual and activation are
-    // applied there and the result leaves as one 16-byte store (bias and residual arrive as
-    // 16-byte loads), instead of 2-byte stores scattered over the tile.
-    constexpr int SROW = T::WN + 8;        // staged row stride in floats (rows 4 apart: 32 banks apart)
-    constexpr int LPR = T::WN / 8;         // lanes per row in the row layout
+    // Row epilogue: a lane owns 8 consecutive columns of a row; the per-row scale, bias, residual
+    // and activation are applied there and the result leaves as one 16-byte store (bias and
+    // residual arrive as 16-byte loads), instead of 2-byte stores scattered over the tile.
+    constexpr int LPR = T::WN / 8;         // lanes per row
     constexpr int RP = 64 / LPR;           // rows per pass
-    float* stg = reinterpret_cast<float*>(smem) + wave * 32 * SROW;
-    const int rl = lane / LPR, c8 = (lane % LPR) * 8;
+    const int c8 = (lane % LPR) * 8;
 #pragma unroll
     for (int i = 0; i < T::FI; ++i) {
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int r = (e >> 2) * 8 + rsub + (e & 3);
-#pragma unroll
-            for (int j = 0; j < T::FJ; ++j) {
-                float v = t.acc[i][j][e];
-                if constexpr (EPI == GEPI_SWIGLU) {
-                    const int row = wm + i * 32 + r;
-                    const float rs = (g.rstd && row < g.M) ? g.rstd[row] : 1.0f;
-                    v = silu_f(v * rs) * t2.acc[i][j][e];
-                }
-                stg[r * SROW + j * 32 + col_in] = v;
-            }
-        }
-        asm volatile("" ::: "memory");
+        stage(i);
 #pragma unroll
         for (int pass = 0; pass < 32 / RP; ++pass) {
-            const int r = pass * RP + rl;
+            const int r = pass * RP + lane / LPR;
             const int row = wm + i * 32 + r;
             const int col = wn + c8;
             if (row >= g.M || col >= g.N) continue;
-            const u32x4 lo = *reinterpret_cast<const u32x4*>(stg + r * SROW + c8);
-            const u32x4 hi = *reinterpret_cast<const u32x4*>(stg + r * SROW + c8 + 4);
-            float y[8] = {__uint_as_float(lo.x), __uint_as_float(lo.y), __uint_as_float(lo.z), __uint_as_float(lo.w),
-                          __uint_as_float(hi.x), __uint_as_float(hi.y), __uint_as_float(hi.z), __uint_as_float(hi.w)};
+            float y[8];
+            ld8(r, c8, y);
             const bool full = col + 8 <= g.N;
             if constexpr (EPI != GEPI_SWIGLU) {
                 const float rs = g.rstd ? g.rstd[row] : 1.0f;
@@ -429,8 +448,7 @@ void gemm_kernel(const GemmArgs g) {
             }
             bf16_t* cp = g.C + (int64_t)row * g.ldc + col;
             if (full) {
-                *reinterpret_cast<u32x4*>(cp) =
-                    u32x4{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]), pack_bf2(y[4], y[5]), pack_bf2(y[6], y[7])};
+                *reinterpret_cast<u32x4*>(cp) = pack8(y);
             } else {
                 for (int q = 0; q < 8 && col + q < g.N; ++q) cp[q] = f2bf(y[q]);
             }
