@@ -13,8 +13,10 @@ tokens, each counted once per layer it passes through).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -27,6 +29,12 @@ if ROOT not in sys.path:
 METRIC = "decode & prefill tokens/s per low-rank layer; % HBM BW / % MFMA peak"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+# HBM bytes per decode-attention call, from counter runs of this script (FETCH_SIZE and
+# WRITE_SIZE, calibrated on a plain copy of known size); valid only for the kernel source whose
+# hash the summary records
+TRAFFIC_NOTE = os.path.join(ROOT, "profiles", "attn_decode_dense_kv_llama7b_b4_hbm_traffic.md")
+ATTN_SRC = os.path.join(ROOT, "svd_compressed_transformer_amd", "csrc", "attention.hip")
+CAL_COPY_BYTES = 256 << 20
 
 
 def log(*a):
@@ -71,6 +79,23 @@ def layer_flops_prefill(cfg, M, r):
     proj = 2 * M * (r["q"] * (d + qd) + r["k"] * (d + kd) + r["v"] * (d + kd) + r["o"] * (qd + d) +
                     r["gate"] * (d + cfg.d_ff) + r["up"] * (d + cfg.d_ff) + r["down"] * (cfg.d_ff + d))
     return proj
+
+
+def recorded_traffic():
+    """Measured HBM bytes per decode-attention call, or None when no summary exists or the kernel
+    source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_NOTE) as f:
+            txt = f.read()
+        with open(ATTN_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    m_sha = re.search(r"attention\.hip sha256: ([0-9a-f]{64})", txt)
+    m_val = re.search(r"traffic_bytes_per_call: (\d+)", txt)
+    if not (m_sha and m_val) or m_sha.group(1) != sha:
+        return None
+    return int(m_val.group(1))
 
 
 # ----------------------------------------------------------------------------- CPU oracle baseline
@@ -211,6 +236,15 @@ def main():
         log(f"warmup {w}: prefill {e[0].elapsed_time(e[1]):.2f} ms, decode {e[1].elapsed_time(e[2]):.2f} ms")
     t_pre_ms = e[0].elapsed_time(e[1])
     t_dec_ms = e[1].elapsed_time(e[2])
+
+    # a plain device copy of known size (256 MiB read, 256 MiB written): the calibration point of
+    # the HBM byte counters in a counter-collection run of this script
+    cal_src = torch.zeros(CAL_COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
+    torch.cuda.empty_cache()
     assert fsvd.fsvd_poll_device_error(dec_ws, stream) == 0
     assert fsvd.fsvd_poll_device_error(pre_ws, stream) == 0
 
@@ -286,7 +320,8 @@ def main():
                    "algorithmic_gbs": round(dec_gbs, 1), "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "kernel": "attn_decode_split (+combine)", "achieved": round(attn_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_us": round(attn_us, 2), "algorithmic_bytes": int(attn_bytes)},
+                     "traffic": recorded_traffic(), "avg_us": round(attn_us, 2),
+                     "algorithmic_bytes": int(attn_bytes), "kv_positions": int(L_mid)},
         "peak_activation_bytes": peak_act,
     }
     if not args.no_cpu:
