@@ -393,45 +393,71 @@ void gemm_kernel(const GemmArgs g) {
 
     // Row epilogue: a lane owns 8 consecutive columns of a row; the per-row scale, bias, residual
     // and activation are applied there and the result leaves as one 16-byte store (bias and
-    // residual arrive as 16-byte loads), instead of 2-byte stores scattered over the tile.
+    // residual arrive as 16-byte loads), instead of 2-byte stores scattered over the tile.  The
+    // residual rows and row scales of the next 32-row block are loaded while the current block is
+    // processed, so the passes do not wait on them one by one.
     constexpr int LPR = T::WN / 8;         // lanes per row
     constexpr int RP = 64 / LPR;           // rows per pass
+    constexpr int NP = 32 / RP;            // passes per 32-row block
     const int c8 = (lane % LPR) * 8;
+    const int col = wn + c8;
+    const bool full = col + 8 <= g.N;
+    float bias8[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) bias8[q] = 0.f;
+    if constexpr (EPI == GEPI_LINEAR) {
+        if (g.bias && col < g.N) {
+            if (full) {
+                const u32x4 bv = *reinterpret_cast<const u32x4*>(g.bias + col);
+                const uint32_t w[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    bias8[2 * q] = bf_lo(w[q]);
+                    bias8[2 * q + 1] = bf_hi(w[q]);
+                }
+            } else {
+                for (int q = 0; q < 8 && col + q < g.N; ++q) bias8[q] = bf2f(g.bias[col + q]);
+            }
+        }
+    }
+    u32x4 resv[2][NP];
+    float rsv[2][NP];
+    auto prefetch = [&](int i, u32x4 (&rv)[NP], float (&rs)[NP]) {
+#pragma unroll
+        for (int pass = 0; pass < NP; ++pass) {
+            const int row = wm + i * 32 + pass * RP + lane / LPR;
+            const bool ok = row < g.M && col < g.N;
+            rs[pass] = (EPI != GEPI_SWIGLU && g.rstd && ok) ? g.rstd[row] : 1.0f;
+            rv[pass] = u32x4{0u, 0u, 0u, 0u};
+            if constexpr (EPI == GEPI_LINEAR) {
+                if (g.residual && ok && full)
+                    rv[pass] = *reinterpret_cast<const u32x4*>(g.residual + (int64_t)row * g.ldr + col);
+            }
+        }
+    };
+    prefetch(0, resv[0], rsv[0]);
 #pragma unroll
     for (int i = 0; i < T::FI; ++i) {
+        if (i + 1 < T::FI) prefetch(i + 1, resv[(i + 1) & 1], rsv[(i + 1) & 1]);
         stage(i);
 #pragma unroll
-        for (int pass = 0; pass < 32 / RP; ++pass) {
+        for (int pass = 0; pass < NP; ++pass) {
             const int r = pass * RP + lane / LPR;
             const int row = wm + i * 32 + r;
-            const int col = wn + c8;
             if (row >= g.M || col >= g.N) continue;
             float y[8];
             ld8(r, c8, y);
-            const bool full = col + 8 <= g.N;
             if constexpr (EPI != GEPI_SWIGLU) {
-                const float rs = g.rstd ? g.rstd[row] : 1.0f;
+                const float rs = rsv[i & 1][pass];
 #pragma unroll
                 for (int q = 0; q < 8; ++q) y[q] *= rs;
             }
             if constexpr (EPI == GEPI_LINEAR) {
-                if (g.bias) {
-                    if (full) {
-                        const u32x4 bv = *reinterpret_cast<const u32x4*>(g.bias + col);
-                        const uint32_t w[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            y[2 * q] += bf_lo(w[q]);
-                            y[2 * q + 1] += bf_hi(w[q]);
-                        }
-                    } else {
-                        for (int q = 0; q < 8 && col + q < g.N; ++q) y[q] += bf2f(g.bias[col + q]);
-                    }
-                }
+                for (int q = 0; q < 8; ++q) y[q] += bias8[q];
                 if (g.residual) {
-                    const bf16_t* rp = g.residual + (int64_t)row * g.ldr + col;
                     if (full) {
-                        const u32x4 rv = *reinterpret_cast<const u32x4*>(rp);
+                        const u32x4 rv = resv[i & 1][pass];
                         const uint32_t w[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
@@ -439,6 +465,7 @@ void gemm_kernel(const GemmArgs g) {
                             y[2 * q + 1] += bf_hi(w[q]);
                         }
                     } else {
+                        const bf16_t* rp = g.residual + (int64_t)row * g.ldr + col;
                         for (int q = 0; q < 8 && col + q < g.N; ++q) y[q] += bf2f(rp[q]);
                     }
                 }
