@@ -20,6 +20,8 @@
 // Sources: fused low-rank projection ("FlashSVD: Memory-Efficient Inference with Streaming for
 // Low-Rank Models", abstract); current-token Q/K/V reconstruction into a dense cache and the
 // packed gate|up projection ("FlashSVD v1.5" explainer, Methodology 2 and 3).
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace fsvd {
@@ -32,6 +34,12 @@ namespace {
 constexpr int kR = FSVD_ROWS;  // factor rows per wave (even)
 constexpr int kH = kR / 2;     // paired units per wave
 constexpr int kMaxWaves = 8; // waves per workgroup (4 or 8, chosen per launch)
+#ifndef FSVD_RD_KPW
+#define FSVD_RD_KPW 1024    // longest reduction slice per wave before the reduction is split
+#endif
+#ifndef FSVD_RD_WAVES
+#define FSVD_RD_WAVES 2048  // the split is doubled while the launch has fewer waves than this
+#endif
 
 template <typename T>
 struct Vec;
@@ -73,18 +81,9 @@ __device__ __forceinline__ float vdot(u32x4 w, u32x4 a, float c, float) {
     return c;
 }
 
-// sum of squares of a 16-byte activation vector (RMSNorm statistics)
-__device__ __forceinline__ float vsq(u32x4 a, bf16_t) {
-    float s = 0.f;
-    uint32_t v[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float lo = bf_lo(v[i]), hi = bf_hi(v[i]);
-        s = fmaf(lo, lo, s);
-        s = fmaf(hi, hi, s);
-    }
-    return s;
-}
+// sum of squares of a 16-byte activation vector (RMSNorm statistics): x . x with v_dot2, added to s
+__device__ __forceinline__ float vsq(u32x4 a, float s, bf16_t) { return vdot(a, a, s, bf16_t()); }
+__device__ __forceinline__ float vsq(u32x4 a, float s, float) { return vdot(a, a, s, float()); }
 // a * w rounded to bf16 (the norm weight applied before the product)
 __device__ __forceinline__ u32x4 vmulw(u32x4 a, u32x4 w) {
     u32x4 r;
@@ -127,7 +126,9 @@ __host__ __device__ __forceinline__ int wave_sets(int epi) { return epi == EPI_S
 template <typename T, int BMAX, int EPI>
 __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const RowdotArgs a) {
     constexpr int E = Vec<T>::E;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index is uniform across the wave; saying so keeps every per-wave quantity (row
+    // pointers, reduction bounds, step counts) in scalar registers and its branches scalar
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int bid = blockIdx.x;
 
     const int si = (a.nseg > 2 && bid >= a.seg[2].blk_begin) ? 2 : ((a.nseg > 1 && bid >= a.seg[1].blk_begin) ? 1 : 0);
@@ -168,11 +169,16 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
         klen[r] = valid ? (mat ? sg.K2 : sg.K) : 0;
         aoff[r] = mat ? sg.act_off2 : sg.act_off;
     }
+    // This wave's slice of the reduction: whole steps of 64 lanes x E elements (one 1 KiB segment
+    // of a row per wave instruction), only the group's last slice can end inside a step.
+    constexpr int SE = 64 * E;
     const int kmax = (EPI == EPI_SWIGLU) ? max(sg.K, sg.K2) : sg.K;
-    const int nvec = kmax / E;
-    const int per = (nvec + ksplit - 1) / ksplit;
-    const int k_lo = ks * per * E;
-    const int k_hi = min(kmax, (ks + 1) * per * E);
+    const int st_per = ((kmax + SE - 1) / SE + ksplit - 1) / ksplit;  // steps per wave
+    const int k_lo = ks * st_per * SE;
+    const int k_hi = min(kmax, k_lo + st_per * SE);
+    const int kw = EPI == EPI_SWIGLU ? (half ? sg.K2 : sg.K) : sg.K;  // length of this wave's rows
+    const int k_end = min(k_hi, kw);                                  // products for k < k_end
+    const int kc_max = kw - E;                                        // clamp for loads past it
 
     float acc[kR][BMAX];
     float ss[BMAX];
@@ -183,47 +189,53 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
         for (int r = 0; r < kR; ++r) acc[r][b] = 0.f;
     }
     const int M = a.M;
-    const char* act = reinterpret_cast<const char*>(a.act);
     const int64_t lda_b = a.lda * (int64_t)sizeof(T);
     const bool norm = (EPI == EPI_Z) && a.norm;
     const bool norm_w = norm && a.norm_w != nullptr;
+    // activation rows past M re-read row M - 1 (their results are never stored); without a norm
+    // weight its loads read the activation instead (valid memory, value unused)
+    const char* arow[BMAX];
+#pragma unroll
+    for (int b = 0; b < BMAX; ++b)
+        arow[b] = reinterpret_cast<const char*>(a.act) + min(b, M - 1) * lda_b + (int64_t)aoff[0] * sizeof(T);
+    const char* nwp = norm_w ? reinterpret_cast<const char*>(a.norm_w) : arow[0];
 
-    // One pass per U steps: every W and activation load of the pass is issued before the first
-    // product (predicated, branch-free), so a wave waits for HBM once per pass.
+    // Passes of up to U steps.  Every load is unconditional (addresses clamped to valid elements),
+    // so all of a pass's loads are in flight before its first product and no lane test or zero
+    // fill runs in the common case; lanes past k_end get a zero activation (a wave's last pass).
     constexpr int U = BMAX <= 2 ? 4 : (BMAX <= 8 ? 2 : 1);
-    const int ka = EPI == EPI_SWIGLU ? (half ? sg.K2 : sg.K) : k_hi;  // activation length
-    for (int kb = k_lo; kb < k_hi; kb += 64 * E * U) {
-        u32x4 wv[U][kR];
-        u32x4 av[U][BMAX];
-        u32x4 nw[U];
+    const int nsteps = k_hi > k_lo ? (k_hi - k_lo + SE - 1) / SE : 0;
+    auto pass = [&](auto nu_c, int s0) {
+        constexpr int NU = decltype(nu_c)::value;  // steps in this pass
+        u32x4 wv[NU][kR];
+        u32x4 av[NU][BMAX];
+        u32x4 nw[NU];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k = kb + (u * 64 + lane) * E;
-            const bool in = k < k_hi;
+        for (int u = 0; u < NU; ++u) {
+            const int k = k_lo + ((s0 + u) * 64 + lane) * E;
+            const int64_t kc = (int64_t)min(k, kc_max) * sizeof(T);
 #pragma unroll
-            for (int r = 0; r < kR; ++r)
-                wv[u][r] = (in && k < klen[r]) ? ldg16_stream(wrow[r] + (int64_t)k * sizeof(T)) : u32x4{0u, 0u, 0u, 0u};
+            for (int r = 0; r < kR; ++r) wv[u][r] = ldg16_stream(wrow[r] + kc);
+            nw[u] = ldg16(nwp + kc);
+#pragma unroll
+            for (int b = 0; b < BMAX; ++b) av[u][b] = ldg16(arow[b] + kc);
         }
+        if (k_lo + (s0 + NU) * SE > k_end) {  // wave-uniform: the pass reaches past k_end
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k = kb + (u * 64 + lane) * E;
-            const bool in = k < k_hi;
-            nw[u] = (norm_w && in) ? ldg16(a.norm_w + k) : u32x4{0u, 0u, 0u, 0u};
+            for (int u = 0; u < NU; ++u) {
+                const bool ok = k_lo + ((s0 + u) * 64 + lane) * E < k_end;
 #pragma unroll
-            for (int b = 0; b < BMAX; ++b) {
-                const bool ok = b < M && in && k < ka;
-                av[u][b] = ok ? ldg16(act + b * lda_b + (int64_t)(aoff[0] + k) * sizeof(T)) : u32x4{0u, 0u, 0u, 0u};
+                for (int b = 0; b < BMAX; ++b) av[u][b] = ok ? av[u][b] : u32x4{0u, 0u, 0u, 0u};
             }
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+        for (int u = 0; u < NU; ++u) {
 #pragma unroll
             for (int b = 0; b < BMAX; ++b) {
-                if (b >= M) continue;
                 u32x4 x = av[u][b];
                 if constexpr (EPI == EPI_Z) {
                     if (norm) {
-                        ss[b] += vsq(x, T());
+                        ss[b] = vsq(x, ss[b], T());
                         if (norm_w) x = vmulw(x, nw[u]);
                     }
                 }
@@ -231,7 +243,11 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
                 for (int r = 0; r < kR; ++r) acc[r][b] = vdot(wv[u][r], x, acc[r][b], T());
             }
         }
-    }
+    };
+    // passes of U steps, then single steps for the rest of the slice (no step past it is loaded)
+    int s0 = 0;
+    for (; s0 + U <= nsteps; s0 += U) pass(std::integral_constant<int, U>(), s0);
+    for (; s0 < nsteps; ++s0) pass(std::integral_constant<int, 1>(), s0);
 
     // lanes -> 4 row partials per value (DPP), then waves/rows combined through LDS
     constexpr int NV = (kR + 1) * BMAX;
@@ -363,8 +379,8 @@ int rowdot_plan(RowdotArgs& a, int epi) {
         units += wave_sets(epi) * (paired ? (u + kH - 1) / kH : (u + kR - 1) / kR);  // waves without split
     }
     int ksplit = 1;
-    while (ksplit < 8 && (kmax + ksplit - 1) / ksplit > 1024 && kmax / (ksplit * 2) >= 256) ksplit *= 2;
-    while (ksplit < 8 && (int64_t)units * ksplit < 2048 && kmax / (ksplit * 2) >= 256) ksplit *= 2;
+    while (ksplit < 8 && (kmax + ksplit - 1) / ksplit > FSVD_RD_KPW && kmax / (ksplit * 2) >= 256) ksplit *= 2;
+    while (ksplit < 8 && (int64_t)units * ksplit < FSVD_RD_WAVES && kmax / (ksplit * 2) >= 256) ksplit *= 2;
     if (a.M > 16) ksplit = std::min(ksplit, 4);  // the 32-row variant runs 4-wave workgroups
     if (epi == EPI_SWIGLU) ksplit = std::min(ksplit, a.M > 16 ? 2 : 4);  // two wave sets per group
     a.ksplit = ksplit;
