@@ -21,6 +21,9 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
+#ifndef FSVD_ATTN_WGS
+#define FSVD_ATTN_WGS 4096  // decode: target workgroups (sequence x kv head x length partition)
+#endif
 
 // EPL: head elements per lane (D / 16): 8 for D = 128, 4 for D = 64.  G: query heads per kv head.
 template <int EPL>
@@ -82,42 +85,62 @@ __global__ __launch_bounds__(256) void attn_decode_split(const AttnArgs a) {
     const bf16_t* kbase = a.kc + ((int64_t)b * a.L_max * a.Hkv + kvh) * D + li * EPL;
     const bf16_t* vbase = a.vc + ((int64_t)b * a.L_max * a.Hkv + kvh) * D + li * EPL;
 
-    // NP positions per lane group per iteration; the K/V vectors of the next iteration are loaded
-    // before the current ones are used, so every wave keeps two iterations of loads in flight
+    // NP positions per lane group per iteration, the same number of iterations for every lane
+    // group (uniform control flow).  The K/V vectors of the next iteration are loaded before the
+    // current ones are used (two iterations in flight per wave); loads are unconditional, rows past
+    // the partition re-read its first row, and such positions get zero weight.  The running max
+    // is updated once per iteration for all NP positions, so the rescale of l and o is paid once.
     constexpr int NP = 2;
     KV<EPL> kv[NP], vv[NP];
     auto load = [&](int64_t jb, KV<EPL> (&kk)[NP], KV<EPL> (&vk)[NP]) {
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int64_t j = jb + 16 * p;
-            const int64_t jj = j < j1 ? j : j0;  // rows past the partition re-read its first row
+            const int64_t jj = j < j1 ? j : j0;
             kk[p] = ld_kv<EPL>(kbase + jj * rowstride);
             vk[p] = ld_kv<EPL>(vbase + jj * rowstride);
         }
     };
-    if (j0 + lg < j1) load(j0 + lg, kv, vv);
-    for (int64_t jb = j0 + lg; jb < j1; jb += 16 * NP) {
+    const int niter = j1 > j0 ? (int)((j1 - j0 + 16 * NP - 1) / (16 * NP)) : 0;  // uniform
+    if (niter > 0) load(j0 + lg, kv, vv);
+    for (int it = 0; it < niter; ++it) {
+        const int64_t jb = j0 + lg + (int64_t)it * 16 * NP;
         KV<EPL> kn[NP], vn[NP];
-        if (jb + 16 * NP < j1) load(jb + 16 * NP, kn, vn);
+        load(jb + 16 * NP, kn, vn);  // past the partition: first row again (cheap, in cache)
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            if (jb + 16 * p >= j1) continue;  // uniform over the lane group (one DPP row)
+        for (int g = 0; g < G; ++g) {
+            float d[NP];
+            bool ok[NP];
+            float mn = m[g];
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float d = 0.f;
+            for (int p = 0; p < NP; ++p) {
+                float t = 0.f;
 #pragma unroll
-                for (int i = 0; i < EPL / 2; ++i) d = dot2bf(qf[g][i], kv[p].w[i], d);
-                d = row16_sum(d) * sc;
-                const float mn = fmaxf(m[g], d);
-                const float alpha = exp2f(m[g] - mn);
-                const float pr = exp2f(d - mn);
-                m[g] = mn;
-                l[g] = l[g] * alpha + pr;
+                for (int i = 0; i < EPL / 2; ++i) t = dot2bf(qf[g][i], kv[p].w[i], t);
+                ok[p] = jb + 16 * p < j1;
+                d[p] = row16_sum(t) * sc;
+                if (ok[p]) mn = fmaxf(mn, d[p]);
+            }
+            const float alpha = exp2f(m[g] - mn);
+            float pr[NP];
+            float lsum = 0.f;
 #pragma unroll
-                for (int i = 0; i < EPL / 2; ++i) {
-                    o[g][2 * i] = o[g][2 * i] * alpha + pr * bf_lo(vv[p].w[i]);
-                    o[g][2 * i + 1] = o[g][2 * i + 1] * alpha + pr * bf_hi(vv[p].w[i]);
+            for (int p = 0; p < NP; ++p) {
+                pr[p] = ok[p] ? exp2f(d[p] - mn) : 0.f;
+                lsum += pr[p];
+            }
+            m[g] = mn;
+            l[g] = l[g] * alpha + lsum;
+#pragma unroll
+            for (int i = 0; i < EPL / 2; ++i) {
+                float lo = o[g][2 * i] * alpha, hi = o[g][2 * i + 1] * alpha;
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    lo = fmaf(pr[p], bf_lo(vv[p].w[i]), lo);
+                    hi = fmaf(pr[p], bf_hi(vv[p].w[i]), hi);
                 }
+                o[g][2 * i] = lo;
+                o[g][2 * i + 1] = hi;
             }
         }
 #pragma unroll
@@ -224,8 +247,8 @@ size_t attn_decode_ws_bytes(int B, int Hq, int D, int nsplit) {
 }
 
 int attn_default_splits(int B, int Hkv, int64_t L_max) {
-    // aim for ~2048 workgroups with at least 64 positions per partition
-    int64_t want = (2048 + (int64_t)B * Hkv - 1) / ((int64_t)B * Hkv);
+    // aim for ~FSVD_ATTN_WGS workgroups with at least 64 positions per partition
+    int64_t want = (FSVD_ATTN_WGS + (int64_t)B * Hkv - 1) / ((int64_t)B * Hkv);
     int64_t cap = (L_max + 63) / 64;
     int64_t s = std::max<int64_t>(1, std::min<int64_t>(want, cap));
     return (int)std::min<int64_t>(s, 64);
