@@ -131,8 +131,11 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int bid = blockIdx.x;
 
-    const int si = (a.nseg > 2 && bid >= a.seg[2].blk_begin) ? 2 : ((a.nseg > 1 && bid >= a.seg[1].blk_begin) ? 1 : 0);
-    const RowdotSeg sg = si == 0 ? a.seg[0] : (si == 1 ? a.seg[1] : a.seg[2]);
+    // only the Q/K/V launch has several segments; the others read segment 0 directly (one round
+    // of argument loads instead of two dependent ones)
+    const int si = EPI != EPI_QKV ? 0
+                   : ((a.nseg > 2 && bid >= a.seg[2].blk_begin) ? 2 : ((a.nseg > 1 && bid >= a.seg[1].blk_begin) ? 1 : 0));
+    const RowdotSeg sg = EPI != EPI_QKV ? a.seg[0] : (si == 0 ? a.seg[0] : (si == 1 ? a.seg[1] : a.seg[2]));
 
     const bool paired = seg_paired(EPI, sg.kind);
     const int upw = paired ? kH : kR;                             // output units per wave
