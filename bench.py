@@ -173,7 +173,7 @@ def main():
         if x0 is None:
             x0 = p["x"]
         pre = DeviceLayer(cfg, p, B=B, S=S, L_max=L_max, kc=None, vc=None, seqlens=np.zeros(B), device=dev,
-                          advance=True, x=np.zeros((B, S, cfg.d), np.float32))
+                          advance=True, x=np.zeros((B, S, cfg.d), np.float32), fold_norm=True)
         del p
         # prefill reads/writes the ping-pong activation buffers and this layer's cache / seqlens
         pre.desc.x = xs_pre[l % 2].data_ptr()

@@ -63,7 +63,7 @@ extern "C" {
 
 typedef struct ihipStream_t* fsvd_stream_t; /* a hipStream_t */
 
-#define FSVD_ABI_VERSION 1
+#define FSVD_ABI_VERSION 2
 
 typedef enum {
     FSVD_OK = 0,
@@ -105,6 +105,16 @@ typedef struct {
 
 fsvd_status_t fsvd_prepack(void* dst, int64_t ld_dst, int64_t cols_pad, const fsvd_pack_item* items /*host*/,
                            int n_items, fsvd_dtype_t dtype, fsvd_stream_t stream);
+
+/* As fsvd_prepack, and every column c < cols[i] of every item is multiplied by col_scale[c]
+ * (device, at least max cols[i] entries, same dtype; product in fp32, bf16 rounded to nearest
+ * even).  Folds an RMSNorm weight w into the input-side factor that follows the norm:
+ * RMSNorm(x) . A^T = rstd(x) * (x . (A diag(w))^T), so a layer built from A diag(w) runs the
+ * norm without its per-element weight multiply (fsvd_decoder_layer_desc flag
+ * FSVD_LAYER_NORM_FOLDED).  Rounding moves from bf16(x * w) to bf16(A * w).  Not timed. */
+fsvd_status_t fsvd_prepack_colscale(void* dst, int64_t ld_dst, int64_t cols_pad,
+                                    const fsvd_pack_item* items /*host*/, int n_items, const void* col_scale,
+                                    fsvd_dtype_t dtype, fsvd_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * a2+a3. Fused low-rank linear  [V1] [V15-M1]
@@ -204,16 +214,20 @@ fsvd_status_t fsvd_seqlens_advance(int32_t* cache_seqlens, int64_t B, int32_t n,
  * appends at cache_seqlens[b]).  Every pointer in the descriptor is a device pointer that the
  * caller keeps alive (and, for a captured graph, at a fixed address) until the last use.
  * ------------------------------------------------------------------------------------------ */
+/* flags: both RMSNorm weights are folded into A_qkv and A_gu (fsvd_prepack_colscale); the layer
+ * applies RMSNorm without a weight and ignores attn_norm_w / mlp_norm_w */
+#define FSVD_LAYER_NORM_FOLDED 0x1
+
 typedef struct fsvd_decoder_layer_desc {
     int64_t B, S, d, Hq, Hkv, D, d_ff, L_max;
     int64_t r_q, r_k, r_v, r_o, r_g, r_u, r_d; /* stored (padded) ranks */
     float norm_eps, rope_theta, softmax_scale;  /* rope_theta 0 -> no RoPE; scale 0 -> 1/sqrt(D) */
     int32_t advance_seqlens;                    /* 1: cache_seqlens += S after the layer */
-    int32_t reserved;
+    int32_t flags;                              /* FSVD_LAYER_* bits, 0 by default */
     const void* x; /* [B, S, d] layer input */
     void* y;       /* [B, S, d] layer output (must not alias x) */
-    const void* attn_norm_w;                    /* [d] */
-    const void* mlp_norm_w;                     /* [d] */
+    const void* attn_norm_w;                    /* [d]; NULL: no norm (ignored when folded) */
+    const void* mlp_norm_w;                     /* [d]; NULL: no norm (ignored when folded) */
     const void* A_qkv;                          /* [r_q + r_k + r_v, d] */
     const void *Vt_q, *Vt_k, *Vt_v;             /* [Hq*D, r_q], [Hkv*D, r_k], [Hkv*D, r_v] */
     const void *Ut_o, *Vt_o;                    /* [r_o, Hq*D], [d, r_o] */

@@ -146,7 +146,8 @@ size_t qkv_scratch(int64_t M, int64_t d, int64_t rtot) {
     return s;
 }
 
-fsvd_status_t enqueue_qkv(const QkvDims& q, const void* x, const void* norm_w, const void* A, const void* Vq,
+// norm: apply RMSNorm to x first; norm_w: its weight, or NULL when the weight is folded into A
+fsvd_status_t enqueue_qkv(const QkvDims& q, const void* x, bool norm, const void* norm_w, const void* A, const void* Vq,
                           const void* Vk, const void* Vv, void* q_out, void* kc, void* vc, const int32_t* seqlens,
                           void* k_out, void* v_out, const QkvBufs& wb, hipStream_t st) {
     const int M = q.B * q.S;
@@ -155,7 +156,7 @@ fsvd_status_t enqueue_qkv(const QkvDims& q, const void* x, const void* norm_w, c
         RowdotArgs a{};
         a.nseg = 1;
         a.act = x; a.lda = q.d; a.M = M; a.err = wb.err;
-        a.norm = norm_w != nullptr; a.norm_w = (const bf16_t*)norm_w; a.norm_eps = q.eps; a.norm_K = q.d;
+        a.norm = norm; a.norm_w = (const bf16_t*)norm_w; a.norm_eps = q.eps; a.norm_K = q.d;
         a.seg[0].W = A; a.seg[0].ldw = q.d; a.seg[0].N = rtot; a.seg[0].K = q.d; a.seg[0].out = wb.z; a.seg[0].ldo = rtot;
         TRY(launch_rowdot(a, EPI_Z, FSVD_BF16, st));
         RowdotArgs b{};
@@ -175,9 +176,10 @@ fsvd_status_t enqueue_qkv(const QkvDims& q, const void* x, const void* norm_w, c
     }
     const bf16_t* a_in = (const bf16_t*)x;
     const float* rstd = nullptr;
-    if (norm_w) {
-        TRY(launch_rms_prep((const bf16_t*)x, (const bf16_t*)norm_w, q.eps, M, q.d, (bf16_t*)wb.xn, wb.rstd, st));
-        a_in = (const bf16_t*)wb.xn;
+    if (norm) {  // rstd per row; the weighted copy x.w only when the weight is not folded into A
+        TRY(launch_rms_prep((const bf16_t*)x, (const bf16_t*)norm_w, q.eps, M, q.d, norm_w ? (bf16_t*)wb.xn : nullptr,
+                            wb.rstd, st));
+        if (norm_w) a_in = (const bf16_t*)wb.xn;
         rstd = wb.rstd;
     }
     GemmArgs g{};
@@ -224,7 +226,7 @@ size_t mlp_scratch(int64_t M, int64_t d, int64_t rgu, int64_t d_ff, int64_t rd) 
     return s;
 }
 
-fsvd_status_t enqueue_mlp(const MlpDims& p, const void* x, const void* norm_w, const void* A_gu, const void* Vg,
+fsvd_status_t enqueue_mlp(const MlpDims& p, const void* x, bool norm, const void* norm_w, const void* A_gu, const void* Vg,
                           const void* Vu, const void* Ud, const void* Vd, const void* residual, void* y,
                           const MlpBufs& wb, int32_t* adv, int advB, int advn, hipStream_t st) {
     const int rgu = p.rg + p.ru;
@@ -232,7 +234,7 @@ fsvd_status_t enqueue_mlp(const MlpDims& p, const void* x, const void* norm_w, c
         RowdotArgs a{};
         a.nseg = 1;
         a.act = x; a.lda = p.d; a.M = p.M; a.err = wb.err;
-        a.norm = norm_w != nullptr; a.norm_w = (const bf16_t*)norm_w; a.norm_eps = p.eps; a.norm_K = p.d;
+        a.norm = norm; a.norm_w = (const bf16_t*)norm_w; a.norm_eps = p.eps; a.norm_K = p.d;
         a.seg[0].W = A_gu; a.seg[0].ldw = p.d; a.seg[0].N = rgu; a.seg[0].K = p.d; a.seg[0].out = wb.z_gu; a.seg[0].ldo = rgu;
         TRY(launch_rowdot(a, EPI_Z, FSVD_BF16, st));
         RowdotArgs b{};
@@ -254,9 +256,10 @@ fsvd_status_t enqueue_mlp(const MlpDims& p, const void* x, const void* norm_w, c
     }
     const bf16_t* a_in = (const bf16_t*)x;
     const float* rstd = nullptr;
-    if (norm_w) {
-        TRY(launch_rms_prep((const bf16_t*)x, (const bf16_t*)norm_w, p.eps, p.M, p.d, (bf16_t*)wb.xn, wb.rstd, st));
-        a_in = (const bf16_t*)wb.xn;
+    if (norm) {
+        TRY(launch_rms_prep((const bf16_t*)x, (const bf16_t*)norm_w, p.eps, p.M, p.d, norm_w ? (bf16_t*)wb.xn : nullptr,
+                            wb.rstd, st));
+        if (norm_w) a_in = (const bf16_t*)wb.xn;
         rstd = wb.rstd;
     }
     GemmArgs g{};
@@ -362,6 +365,7 @@ fsvd_status_t validate_layer(const fsvd_decoder_layer_desc* d) {
                         "Ut_d", "Vt_d", "k_cache", "v_cache", "ws"};
     for (size_t i = 0; i < sizeof(ptrs) / sizeof(ptrs[0]); ++i) TRY(need_ptr(ptrs[i], pn[i]));
     TRY(opt_ptr(d->attn_norm_w, "attn_norm_w")); TRY(opt_ptr(d->mlp_norm_w, "mlp_norm_w"));
+    if (d->flags & ~FSVD_LAYER_NORM_FOLDED) return fail(FSVD_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)d->flags);
     if (!d->cache_seqlens) return fail(FSVD_ERR_INVALID_ARG, "cache_seqlens is NULL");
     if (d->x == d->y) return fail(FSVD_ERR_INVALID_ARG, "y must not alias x");
     if (d->S > d->L_max) return fail(FSVD_ERR_INVALID_ARG, "S (%lld) exceeds L_max", (long long)d->S);
@@ -376,7 +380,8 @@ fsvd_status_t enqueue_layer(const fsvd_decoder_layer_desc* d, hipStream_t st) {
     const int B = (int)d->B, S = (int)d->S, M = B * S;
     QkvDims qd{B, S, (int)d->d, (int)d->r_q, (int)d->r_k, (int)d->r_v, (int)d->Hq, (int)d->Hkv, (int)d->D,
                d->L_max, d->norm_eps, d->rope_theta};
-    TRY(enqueue_qkv(qd, d->x, d->attn_norm_w, d->A_qkv, d->Vt_q, d->Vt_k, d->Vt_v, p.q, d->k_cache, d->v_cache,
+    const bool folded = (d->flags & FSVD_LAYER_NORM_FOLDED) != 0;
+    TRY(enqueue_qkv(qd, d->x, folded || d->attn_norm_w != nullptr, folded ? nullptr : d->attn_norm_w, d->A_qkv, d->Vt_q, d->Vt_k, d->Vt_v, p.q, d->k_cache, d->v_cache,
                     d->cache_seqlens, nullptr, nullptr, p.qb, st));
     TRY(enqueue_attn(p.q, d->k_cache, d->v_cache, d->L_max, d->cache_seqlens, B, S, (int)d->Hq, (int)d->Hkv,
                      (int)d->D, d->softmax_scale, 1, p.o, p.attn_part, p.nsplit, p.qb.err, st));
@@ -385,7 +390,7 @@ fsvd_status_t enqueue_layer(const fsvd_decoder_layer_desc* d, hipStream_t st) {
     TRY(enqueue_linear(p.o, M, qdim, qdim, d->Ut_o, (int)d->r_o, qdim, d->Vt_o, (int)d->d, d->r_o, nullptr, d->x, d->d,
                        p.h, d->d, FSVD_BF16, lb, nullptr, 0, 0, st));
     MlpDims md{M, (int)d->d, (int)d->r_g, (int)d->r_u, (int)d->d_ff, (int)d->r_d, d->norm_eps, FSVD_ACT_SWIGLU};
-    return enqueue_mlp(md, p.h, d->mlp_norm_w, d->A_gu, d->Vt_g, d->Vt_u, d->Ut_d, d->Vt_d, p.h, d->y, p.mb,
+    return enqueue_mlp(md, p.h, folded || d->mlp_norm_w != nullptr, folded ? nullptr : d->mlp_norm_w, d->A_gu, d->Vt_g, d->Vt_u, d->Ut_d, d->Vt_d, p.h, d->y, p.mb,
                        d->advance_seqlens ? d->cache_seqlens : nullptr, B, S, st);
 }
 
@@ -406,6 +411,11 @@ struct fsvd_graph {
 
 using namespace fsvd;
 
+namespace {
+fsvd_status_t prepack_impl(void* dst, int64_t ld_dst, int64_t cols_pad, const fsvd_pack_item* items, int n_items,
+                           const void* col_scale, fsvd_dtype_t dtype, fsvd_stream_t stream);
+}  // namespace
+
 extern "C" {
 
 int fsvd_abi_version(void) { return FSVD_ABI_VERSION; }
@@ -425,8 +435,23 @@ const char* fsvd_status_str(fsvd_status_t s) {
 
 const char* fsvd_last_error(void) { return g_err; }
 
+
 fsvd_status_t fsvd_prepack(void* dst, int64_t ld_dst, int64_t cols_pad, const fsvd_pack_item* items, int n_items,
                            fsvd_dtype_t dtype, fsvd_stream_t stream) {
+    return prepack_impl(dst, ld_dst, cols_pad, items, n_items, nullptr, dtype, stream);
+}
+
+fsvd_status_t fsvd_prepack_colscale(void* dst, int64_t ld_dst, int64_t cols_pad, const fsvd_pack_item* items,
+                                    int n_items, const void* col_scale, fsvd_dtype_t dtype, fsvd_stream_t stream) {
+    TRY(need_ptr(col_scale, "col_scale"));
+    return prepack_impl(dst, ld_dst, cols_pad, items, n_items, col_scale, dtype, stream);
+}
+
+}  // extern "C"
+
+namespace {
+fsvd_status_t prepack_impl(void* dst, int64_t ld_dst, int64_t cols_pad, const fsvd_pack_item* items, int n_items,
+                           const void* col_scale, fsvd_dtype_t dtype, fsvd_stream_t stream) {
     TRY(need_dtype(dtype, true));
     if (!dst) return fail(FSVD_ERR_INVALID_ARG, "dst is NULL");
     if (!items || n_items <= 0) return fail(FSVD_ERR_INVALID_ARG, "no items");
@@ -442,11 +467,14 @@ fsvd_status_t fsvd_prepack(void* dst, int64_t ld_dst, int64_t cols_pad, const fs
     for (int i = 0; i < n_items; ++i) {
         const fsvd_pack_item& it = items[i];
         TRY(launch_prepack(dst, ld_dst, cols_pad, row, it.src, it.rows, it.cols, it.ld_src, it.rows_pad, esize(dtype),
-                           (hipStream_t)stream));
+                           col_scale, (hipStream_t)stream));
         row += it.rows_pad;
     }
     return FSVD_OK;
 }
+}  // namespace
+
+extern "C" {
 
 size_t fsvd_lowrank_linear_ws(int64_t M, int64_t K, int64_t r, int64_t N, fsvd_dtype_t dtype) {
     (void)K; (void)N;
@@ -509,7 +537,7 @@ fsvd_status_t fsvd_lowrank_qkv(const void* x, int64_t B, int64_t S, int64_t d, c
     }
     qb.err = (int*)ws;
     QkvDims qd{(int)B, (int)S, (int)d, (int)r_q, (int)r_k, (int)r_v, (int)Hq, (int)Hkv, (int)D, L_max, norm_eps, rope_theta};
-    return enqueue_qkv(qd, x, norm_w, A_qkv, Vt_q, Vt_k, Vt_v, q_out, k_cache, v_cache, cache_seqlens, k_out, v_out, qb,
+    return enqueue_qkv(qd, x, norm_w != nullptr, norm_w, A_qkv, Vt_q, Vt_k, Vt_v, q_out, k_cache, v_cache, cache_seqlens, k_out, v_out, qb,
                        (hipStream_t)stream);
 }
 
@@ -550,7 +578,7 @@ fsvd_status_t fsvd_lowrank_mlp_packed(const void* x, int64_t M, int64_t d, const
     }
     mb.err = (int*)ws;
     MlpDims md{(int)M, (int)d, (int)r_g, (int)r_u, (int)d_ff, (int)r_d, norm_eps, act};
-    return enqueue_mlp(md, x, norm_w, A_gu, Vt_g, Vt_u, Ut_d, Vt_d, residual, y, mb, nullptr, 0, 0, (hipStream_t)stream);
+    return enqueue_mlp(md, x, norm_w != nullptr, norm_w, A_gu, Vt_g, Vt_u, Ut_d, Vt_d, residual, y, mb, nullptr, 0, 0, (hipStream_t)stream);
 }
 
 size_t fsvd_decode_attn_dense_kv_ws(int64_t B, int64_t Sq, int64_t Hq, int64_t Hkv, int64_t D, int64_t L_max) {

@@ -264,11 +264,7 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int* tm, i
 }
 
 template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(kThreads, 1)
-#if defined(FSVD_GEMM_WPE)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
-#endif
-void gemm_kernel(const GemmArgs g) {
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
     extern __shared__ u32x4 smem[];
     using T = Tile<BM, BN>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -349,7 +345,7 @@ void gemm_kernel(const GemmArgs g) {
         __syncthreads();
         bf16_t* dst = g.seg == 0 ? g.q_out : (g.seg == 1 ? g.k_cache : g.v_cache);
         bf16_t* dbg = g.seg == 1 ? g.k_out : (g.seg == 2 ? g.v_out : nullptr);
-#pragma unroll
+#pragma unroll 1
         for (int i = 0; i < T::FI; ++i) {
             stage(i);
 #pragma unroll

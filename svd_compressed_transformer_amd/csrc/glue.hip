@@ -10,11 +10,20 @@ namespace {
 // [row0, row0 + rows_pad) x [0, cols_pad), zero-filling the pad area.  One thread per element.
 template <typename E>
 __global__ void prepack_kernel(E* dst, int64_t ld_dst, int64_t cols_pad, int64_t row0, const E* src, int64_t rows,
-                               int64_t cols, int64_t ld_src, int64_t rows_pad) {
+                               int64_t cols, int64_t ld_src, int64_t rows_pad, const E* col_scale) {
     const int64_t total = rows_pad * cols_pad;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t r = i / cols_pad, c = i - r * cols_pad;
-        dst[(row0 + r) * ld_dst + c] = (r < rows && c < cols) ? src[r * ld_src + c] : E(0);
+        E v = (r < rows && c < cols) ? src[r * ld_src + c] : E(0);
+        if (col_scale != nullptr && c < cols) {
+            // column c scaled by col_scale[c] in fp32, rounded to nearest even
+            if constexpr (sizeof(E) == 2) {
+                v = f2bf(bf2f(v) * bf2f(col_scale[c]));
+            } else {
+                v = __float_as_uint(__uint_as_float(v) * __uint_as_float(col_scale[c]));
+            }
+        }
+        dst[(row0 + r) * ld_dst + c] = v;
     }
 }
 
@@ -65,7 +74,7 @@ __global__ __launch_bounds__(256) void rms_prep_kernel(const bf16_t* x, const bf
     for (int64_t i = threadIdx.x; i < d; i += 256) {
         const float v = bf2f(xr[i]);
         s += v * v;
-        xn[row * d + i] = w ? f2bf(v * bf2f(w[i])) : xr[i];
+        if (xn) xn[row * d + i] = w ? f2bf(v * bf2f(w[i])) : xr[i];
     }
     s = wave_sum(s);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
@@ -76,16 +85,17 @@ __global__ __launch_bounds__(256) void rms_prep_kernel(const bf16_t* x, const bf
 }  // namespace
 
 fsvd_status_t launch_prepack(void* dst, int64_t ld_dst, int64_t cols_pad, int64_t row0, const void* src, int64_t rows,
-                             int64_t cols, int64_t ld_src, int64_t rows_pad, size_t es, hipStream_t st) {
+                             int64_t cols, int64_t ld_src, int64_t rows_pad, size_t es, const void* col_scale,
+                             hipStream_t st) {
     const int64_t total = rows_pad * cols_pad;
     if (total == 0) return FSVD_OK;
     const int grid = (int)std::min<int64_t>((total + 255) / 256, 65536);
     if (es == 2)
         prepack_kernel<uint16_t><<<grid, 256, 0, st>>>((uint16_t*)dst, ld_dst, cols_pad, row0, (const uint16_t*)src,
-                                                        rows, cols, ld_src, rows_pad);
+                                                        rows, cols, ld_src, rows_pad, (const uint16_t*)col_scale);
     else
         prepack_kernel<uint32_t><<<grid, 256, 0, st>>>((uint32_t*)dst, ld_dst, cols_pad, row0, (const uint32_t*)src,
-                                                        rows, cols, ld_src, rows_pad);
+                                                        rows, cols, ld_src, rows_pad, (const uint32_t*)col_scale);
     return check_launch("prepack");
 }
 

@@ -87,8 +87,9 @@ fsvd_status_t launch_attn_decode(const AttnArgs& a, hipStream_t st);
 fsvd_status_t launch_attn_prefill(const AttnArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------- glue
-fsvd_status_t launch_prepack(void* dst, int64_t ld_dst, int64_t cols_pad, int64_t row0, const void* src,
-                             int64_t rows, int64_t cols, int64_t ld_src, int64_t rows_pad, size_t es, hipStream_t st);
+fsvd_status_t launch_prepack(void* dst, int64_t ld_dst, int64_t cols_pad, int64_t row0, const void* src, int64_t rows,
+                             int64_t cols, int64_t ld_src, int64_t rows_pad, size_t es, const void* col_scale,
+                             hipStream_t st);
 fsvd_status_t launch_layernorm(const bf16_t* x, const bf16_t* res, const bf16_t* g, const bf16_t* b, float eps,
                                int64_t M, int64_t d, bf16_t* y, hipStream_t st);
 fsvd_status_t launch_seqlens_advance(int32_t* sl, int64_t B, int32_t n, hipStream_t st);

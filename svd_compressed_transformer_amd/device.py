@@ -26,13 +26,17 @@ def bits(t) -> np.ndarray:
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def pack_rows_dev(blocks, pad=PAD, device="cuda"):
-    """Stack device bf16 blocks [r_i, K] into one [sum(pad(r_i)), K] tensor with fsvd_prepack."""
+def pack_rows_dev(blocks, pad=PAD, device="cuda", col_scale=None):
+    """Stack device bf16 blocks [r_i, K] into one [sum(pad(r_i)), K] tensor with fsvd_prepack
+    (with fsvd_prepack_colscale when col_scale [K] is given: column c scaled by col_scale[c])."""
     K = blocks[0].shape[1]
     rp = [round_up(b.shape[0], pad) for b in blocks]
     dst = torch.empty((sum(rp), K), dtype=blocks[0].dtype, device=device)
     items = [(b, b.shape[0], K, b.stride(0), r) for b, r in zip(blocks, rp)]
-    fsvd.fsvd_prepack(dst, K, K, items, fsvd.dtype_of(blocks[0]))
+    if col_scale is None:
+        fsvd.fsvd_prepack(dst, K, K, items, fsvd.dtype_of(blocks[0]))
+    else:
+        fsvd.fsvd_prepack_colscale(dst, K, K, items, col_scale, fsvd.dtype_of(blocks[0]))
     return dst, rp
 
 
@@ -47,23 +51,27 @@ def pad_cols_dev(m, cols_pad, device="cuda"):
 class DeviceLayer:
     """One Llama-style low-rank decoder layer resident on the GPU (factors packed and padded)."""
 
-    def __init__(self, cfg, p, B, S, L_max, kc, vc, seqlens, device="cuda", advance=False, x=None):
+    def __init__(self, cfg, p, B, S, L_max, kc, vc, seqlens, device="cuda", advance=False, x=None, fold_norm=False):
+        """fold_norm: fold both RMSNorm weights into A_qkv and A_gu at packing time and run the layer
+        with FSVD_LAYER_NORM_FOLDED."""
         self.cfg, self.B, self.S, self.L_max = cfg, B, S, L_max
         dev = device
         up = {k: to_dev(v, device=dev) for k, v in p.items() if k.startswith(("Ut_", "Vt_"))}
-        self.A_qkv, (rq, rk, rv) = pack_rows_dev([up["Ut_q"], up["Ut_k"], up["Ut_v"]], device=dev)
+        self.attn_norm_w = to_dev(p["attn_norm_w"], device=dev)
+        self.mlp_norm_w = to_dev(p["mlp_norm_w"], device=dev)
+        self.A_qkv, (rq, rk, rv) = pack_rows_dev([up["Ut_q"], up["Ut_k"], up["Ut_v"]], device=dev,
+                                                 col_scale=self.attn_norm_w if fold_norm else None)
         self.Vt_q, self.Vt_k, self.Vt_v = (pad_cols_dev(up["Vt_q"], rq, dev), pad_cols_dev(up["Vt_k"], rk, dev),
                                            pad_cols_dev(up["Vt_v"], rv, dev))
         self.Ut_o, (ro,) = pack_rows_dev([up["Ut_o"]], device=dev)
         self.Vt_o = pad_cols_dev(up["Vt_o"], ro, dev)
-        self.A_gu, (rg, ru) = pack_rows_dev([up["Ut_gate"], up["Ut_up"]], device=dev)
+        self.A_gu, (rg, ru) = pack_rows_dev([up["Ut_gate"], up["Ut_up"]], device=dev,
+                                            col_scale=self.mlp_norm_w if fold_norm else None)
         self.Vt_g, self.Vt_u = pad_cols_dev(up["Vt_gate"], rg, dev), pad_cols_dev(up["Vt_up"], ru, dev)
         self.Ut_d, (rd,) = pack_rows_dev([up["Ut_down"]], device=dev)
         self.Vt_d = pad_cols_dev(up["Vt_down"], rd, dev)
         del up
         self.ranks = dict(r_q=rq, r_k=rk, r_v=rv, r_o=ro, r_g=rg, r_u=ru, r_d=rd)
-        self.attn_norm_w = to_dev(p["attn_norm_w"], device=dev)
-        self.mlp_norm_w = to_dev(p["mlp_norm_w"], device=dev)
         self.x = to_dev(p["x"] if x is None else x, device=dev).reshape(B, S, cfg.d).contiguous()
         self.y = torch.empty_like(self.x)
         self.k_cache = to_dev(kc, device=dev) if kc is not None else torch.zeros(
@@ -73,6 +81,7 @@ class DeviceLayer:
         self.desc = fsvd.decoder_layer_desc(
             B=B, S=S, d=cfg.d, Hq=cfg.Hq, Hkv=cfg.Hkv, D=cfg.D, d_ff=cfg.d_ff, L_max=L_max, **self.ranks,
             norm_eps=cfg.norm_eps, rope_theta=cfg.rope_theta, softmax_scale=0.0, advance_seqlens=int(advance),
+            flags=fsvd.FSVD_LAYER_NORM_FOLDED if fold_norm else 0,
             x=self.x, y=self.y, attn_norm_w=self.attn_norm_w, mlp_norm_w=self.mlp_norm_w, A_qkv=self.A_qkv,
             Vt_q=self.Vt_q, Vt_k=self.Vt_k, Vt_v=self.Vt_v, Ut_o=self.Ut_o, Vt_o=self.Vt_o, A_gu=self.A_gu,
             Vt_g=self.Vt_g, Vt_u=self.Vt_u, Ut_d=self.Ut_d, Vt_d=self.Vt_d, k_cache=self.k_cache,

@@ -16,6 +16,7 @@ FSVD_ERR_HIP, FSVD_ERR_CAPTURE, FSVD_ERR_DEVICE = 4, 5, 6
 FSVD_F32, FSVD_BF16 = 0, 1
 FSVD_ACT_SWIGLU, FSVD_ACT_GELU = 0, 1
 FSVD_DEVERR_KV_OVERFLOW, FSVD_DEVERR_SEQ_OVERFLOW = 0x1, 0x2
+FSVD_LAYER_NORM_FOLDED = 0x1
 
 _i64, _sz, _vp, _f32, _i32 = C.c_int64, C.c_size_t, C.c_void_p, C.c_float, C.c_int32
 
@@ -34,7 +35,7 @@ class DecoderLayerDesc(C.Structure):
     _fields_ = [(n, _i64) for n in ("B", "S", "d", "Hq", "Hkv", "D", "d_ff", "L_max",
                                      "r_q", "r_k", "r_v", "r_o", "r_g", "r_u", "r_d")] + [
         ("norm_eps", _f32), ("rope_theta", _f32), ("softmax_scale", _f32),
-        ("advance_seqlens", _i32), ("reserved", _i32)] + [
+        ("advance_seqlens", _i32), ("flags", _i32)] + [
         (n, _vp) for n in ("x", "y", "attn_norm_w", "mlp_norm_w", "A_qkv", "Vt_q", "Vt_k", "Vt_v", "Ut_o", "Vt_o",
                            "A_gu", "Vt_g", "Vt_u", "Ut_d", "Vt_d", "k_cache", "v_cache", "cache_seqlens", "ws")] + [
         ("ws_bytes", _sz)]
@@ -45,6 +46,7 @@ _SIGS = {
     "fsvd_status_str": (C.c_char_p, [C.c_int]),
     "fsvd_last_error": (C.c_char_p, []),
     "fsvd_prepack": (C.c_int, [_vp, _i64, _i64, C.POINTER(PackItem), C.c_int, C.c_int, _vp]),
+    "fsvd_prepack_colscale": (C.c_int, [_vp, _i64, _i64, C.POINTER(PackItem), C.c_int, _vp, C.c_int, _vp]),
     "fsvd_lowrank_linear_ws": (_sz, [_i64, _i64, _i64, _i64, C.c_int]),
     "fsvd_lowrank_linear": (C.c_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64,
                                       _vp, _i64, C.c_int, _vp, _sz, _vp]),
@@ -143,6 +145,12 @@ def fsvd_prepack(dst, ld_dst, cols_pad, items, dtype, stream=None):
     """items: sequence of (src_tensor, rows, cols, ld_src, rows_pad)."""
     arr = (PackItem * len(items))(*[PackItem(_p(s), r, c, ld, rp) for (s, r, c, ld, rp) in items])
     _check(lib().fsvd_prepack(_p(dst), ld_dst, cols_pad, arr, len(items), dtype, _s(stream)))
+
+
+def fsvd_prepack_colscale(dst, ld_dst, cols_pad, items, col_scale, dtype, stream=None):
+    """As fsvd_prepack, every column c scaled by col_scale[c] (folds an RMSNorm weight into A)."""
+    arr = (PackItem * len(items))(*[PackItem(_p(s), r, c, ld, rp) for (s, r, c, ld, rp) in items])
+    _check(lib().fsvd_prepack_colscale(_p(dst), ld_dst, cols_pad, arr, len(items), _p(col_scale), dtype, _s(stream)))
 
 
 def fsvd_lowrank_linear_ws(M, K, r, N, dtype) -> int:

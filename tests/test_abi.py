@@ -37,7 +37,9 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert fsvd.fsvd_abi_version() == 1
+    import re
+    hdr = open(os.path.join(ROOT, "include", "fsvd.h")).read()
+    assert fsvd.fsvd_abi_version() == int(re.search(r"#define FSVD_ABI_VERSION (\d+)", hdr).group(1))
     assert fsvd.fsvd_status_str(0) == "ok"
     assert "workspace" in fsvd.fsvd_status_str(fsvd.FSVD_ERR_WORKSPACE)
 

@@ -53,6 +53,21 @@ def test_prepack_bit_exact():
     assert np.array_equal(dst.cpu().numpy(), exp)
 
 
+def test_prepack_colscale_bit_exact():
+    """Packing with a column scale (the RMSNorm weight folded into A): each element is the bf16
+    rounding (nearest even) of the exact fp32 product of two bf16 values; padding stays zero."""
+    rng = np.random.default_rng(1)
+    K = 200
+    blocks = [I.round_bf16(rng.standard_normal((r, K))) for r in (13, 8)]
+    w = I.round_bf16(1.0 + 0.1 * rng.standard_normal(K))
+    say("prepack with column scale", [b.shape for b in blocks])
+    packed, rp = pack_rows_dev([to_dev(b) for b in blocks], col_scale=to_dev(w))
+    ref, _ = O.pack_rows(blocks, pad_to=8)
+    exp = I.bf16_bits(ref.astype(np.float32) * w.astype(np.float32)[None, :])
+    assert rp == [16, 8]
+    assert np.array_equal(bits(packed), exp)
+
+
 # ----------------------------------------------------------------------------- low-rank linear (a2 + a3)
 
 

@@ -31,13 +31,16 @@ SMALL_GQA = I.scaled_decoder(I.CFG4, d=512, Hq=8, Hkv=2, D=128, d_ff=1024,
                              ranks={"q": 256, "k": 128, "v": 64, "o": 192, "gate": 128, "up": 256, "down": 96})
 
 
-@pytest.mark.parametrize("cfg,B,L0", [(SMALL, 1, 0), (SMALL, 3, 45), (SMALL_GQA, 4, 130), (SMALL_GQA, 32, 17)])
-def test_decode_layer_eager(cfg, B, L0):
+@pytest.mark.parametrize("cfg,B,L0,fold", [(SMALL, 1, 0, False), (SMALL, 3, 45, False), (SMALL_GQA, 4, 130, False),
+                                            (SMALL_GQA, 32, 17, False), (SMALL, 3, 45, True), (SMALL_GQA, 32, 17, True)])
+def test_decode_layer_eager(cfg, B, L0, fold):
+    """fold: RMSNorm weights folded into A_qkv / A_gu (FSVD_LAYER_NORM_FOLDED); the oracle keeps
+    them separate."""
     L_max = 160
-    say("decode layer eager", cfg.name, B, L0)
+    say("decode layer eager", cfg.name, B, L0, "folded" if fold else "")
     p = I.make_decoder_layer(cfg, B=B, S=1, seed=B, random_norm_weights=True)
     kc, vc = I.make_kv_history(B, L_max, cfg.Hkv, cfg.D, L0, seed=11)
-    lay = DeviceLayer(cfg, p, B=B, S=1, L_max=L_max, kc=kc, vc=vc, seqlens=np.full(B, L0))
+    lay = DeviceLayer(cfg, p, B=B, S=1, L_max=L_max, kc=kc, vc=vc, seqlens=np.full(B, L0), fold_norm=fold)
     lay.run()
     torch.cuda.synchronize()
     y_ref, kc_ref, vc_ref = O.decoder_layer(p["x"], p, cfg, kc, vc, np.full(B, L0))
@@ -46,13 +49,14 @@ def test_decode_layer_eager(cfg, B, L0):
     assert fsvd.fsvd_poll_device_error(lay.ws) == 0
 
 
-def test_prefill_layer_small_rowdot_path():
+@pytest.mark.parametrize("fold", [False, True])
+def test_prefill_layer_small_rowdot_path(fold):
     """S > 1 with M = B*S <= 32 exercises the row-dot kernels with several tokens per sequence."""
     cfg = SMALL_GQA
     B, S, L_max = 2, 5, 64
-    say("prefill layer (row-dot sizes)")
+    say("prefill layer (row-dot sizes)", "folded" if fold else "")
     p = I.make_decoder_layer(cfg, B=B, S=S, seed=21, random_norm_weights=True)
-    lay = DeviceLayer(cfg, p, B=B, S=S, L_max=L_max, kc=None, vc=None, seqlens=[0, 9])
+    lay = DeviceLayer(cfg, p, B=B, S=S, L_max=L_max, kc=None, vc=None, seqlens=[0, 9], fold_norm=fold)
     lay.run()
     torch.cuda.synchronize()
     z = np.zeros((B, L_max, cfg.Hkv, cfg.D))
@@ -60,17 +64,19 @@ def test_prefill_layer_small_rowdot_path():
     assert rel(lay.y_host(), y_ref) <= BF16_TOL
 
 
-@pytest.mark.parametrize("cfg,B", [(SMALL, 2), (SMALL_GQA, 4)])
-def test_graph_replay_equals_eager_and_oracle(cfg, B):
+@pytest.mark.parametrize("cfg,B,fold", [(SMALL, 2, False), (SMALL_GQA, 4, False), (SMALL_GQA, 4, True)])
+def test_graph_replay_equals_eager_and_oracle(cfg, B, fold):
     L_max, L0, N = 96, 20, 6
-    say("graph replay", cfg.name, B)
+    say("graph replay", cfg.name, B, "folded" if fold else "")
     p = I.make_decoder_layer(cfg, B=B, S=1, seed=5, random_norm_weights=True)
     kc, vc = I.make_kv_history(B, L_max, cfg.Hkv, cfg.D, L0, seed=12)
     rng = np.random.default_rng(99)
     xs = I.round_bf16(rng.standard_normal((N, B, cfg.d)))
 
-    eager = DeviceLayer(cfg, p, B=B, S=1, L_max=L_max, kc=kc, vc=vc, seqlens=np.full(B, L0), advance=True)
-    graph_l = DeviceLayer(cfg, p, B=B, S=1, L_max=L_max, kc=kc, vc=vc, seqlens=np.full(B, L0), advance=True)
+    eager = DeviceLayer(cfg, p, B=B, S=1, L_max=L_max, kc=kc, vc=vc, seqlens=np.full(B, L0), advance=True,
+                        fold_norm=fold)
+    graph_l = DeviceLayer(cfg, p, B=B, S=1, L_max=L_max, kc=kc, vc=vc, seqlens=np.full(B, L0), advance=True,
+                          fold_norm=fold)
     g = graph_l.capture()
     try:
         ys_e, ys_g = [], []

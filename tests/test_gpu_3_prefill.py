@@ -109,12 +109,13 @@ def test_mlp_prefill_swiglu(M):
     assert rel(from_dev(y), ref) <= BF16_TOL
 
 
-def test_decoder_prefill_layer():
+@pytest.mark.parametrize("fold", [False, True])
+def test_decoder_prefill_layer(fold):
     cfg = SMALL
     B, S, L_max = 2, 150, 200
-    say("decoder prefill layer", B, S)
+    say("decoder prefill layer", B, S, "folded" if fold else "")
     p = I.make_decoder_layer(cfg, B=B, S=S, seed=77, random_norm_weights=True)
-    lay = DeviceLayer(cfg, p, B=B, S=S, L_max=L_max, kc=None, vc=None, seqlens=[0, 30])
+    lay = DeviceLayer(cfg, p, B=B, S=S, L_max=L_max, kc=None, vc=None, seqlens=[0, 30], fold_norm=fold)
     lay.run()
     torch.cuda.synchronize()
     z = np.zeros((B, L_max, cfg.Hkv, cfg.D))

@@ -9,8 +9,10 @@
   over a history of 8192 tokens.
 - The benchmark's prefill + decode sequence: a 4 x 2048-token prefill of the 7B-shaped layer
   (MFMA path, eager), then decode steps replayed from the captured graph with the in-graph
-  length advance.  The oracle runs its own prefill (never the GPU's): the whole K/V cache it
-  writes is compared, the layer output on sampled rows, and the replayed decode outputs.
+  length advance, with the RMSNorm weights folded into A_qkv / A_gu as the benchmark packs
+  them.  The oracle runs its own prefill (never the GPU's), with the weights kept separate: the
+  whole K/V cache it writes is compared, the layer output on sampled rows, and the replayed
+  decode outputs.
 - BERT-Base-shaped encoder layer (768, 12 x 64, d_ff 3072, rank 384), batch 8 x 512: whole output.
 """
 import ctypes
@@ -104,7 +106,7 @@ def test_llama7b_prefill_then_replayed_decode_full():
     p = I.make_decoder_layer(cfg, B=B, S=S, seed=8, random_norm_weights=True)
     nan_cache = np.full((B, L_max, cfg.Hkv, cfg.D), np.nan, dtype=np.float32)
     pre = DeviceLayer(cfg, p, B=B, S=S, L_max=L_max, kc=nan_cache, vc=nan_cache, seqlens=np.zeros(B),
-                      advance=True)
+                      advance=True, fold_norm=True)
     del nan_cache
     pre.run()
     torch.cuda.synchronize()
