@@ -248,7 +248,13 @@ fsvd_status_t fsvd_decoder_layer_run(const fsvd_decoder_layer_desc* desc /*host*
 /* Captures the layer (S must be 1) into a hipGraph on a library-owned capture stream and
  * instantiates it; synchronises the device once.  *out receives the graph handle (host). */
 fsvd_status_t fsvd_decoder_layer_capture(const fsvd_decoder_layer_desc* desc /*host*/, fsvd_graph** out);
-/* One hipGraphLaunch of the captured layer on stream. */
+/* As fsvd_decoder_layer_capture for n_layers descriptors (host array) enqueued in order into ONE
+ * graph: a whole decode step of a layer stack replayed with one hipGraphLaunch (the caller chains
+ * layer l's y to layer l+1's x).  The per-layer graph is the pages' design; this variant removes
+ * the per-graph launch boundary between layers. */
+fsvd_status_t fsvd_decoder_stack_capture(const fsvd_decoder_layer_desc* descs /*host*/, int n_layers,
+                                         fsvd_graph** out);
+/* One hipGraphLaunch of the captured layer (or stack) on stream. */
 fsvd_status_t fsvd_graph_replay(fsvd_graph* g, fsvd_stream_t stream);
 fsvd_status_t fsvd_graph_destroy(fsvd_graph* g);
 

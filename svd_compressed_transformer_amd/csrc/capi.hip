@@ -637,10 +637,17 @@ fsvd_status_t fsvd_decoder_layer_run(const fsvd_decoder_layer_desc* desc, fsvd_s
 }
 
 fsvd_status_t fsvd_decoder_layer_capture(const fsvd_decoder_layer_desc* desc, fsvd_graph** out) {
+    return fsvd_decoder_stack_capture(desc, 1, out);
+}
+
+fsvd_status_t fsvd_decoder_stack_capture(const fsvd_decoder_layer_desc* descs, int n_layers, fsvd_graph** out) {
     if (!out) return fail(FSVD_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
-    TRY(validate_layer(desc));
-    if (desc->S != 1) return fail(FSVD_ERR_UNSUPPORTED, "graph capture is for single-token decode steps (S == 1)");
+    if (!descs || n_layers <= 0) return fail(FSVD_ERR_INVALID_ARG, "no layers");
+    for (int l = 0; l < n_layers; ++l) {
+        TRY(validate_layer(&descs[l]));
+        if (descs[l].S != 1) return fail(FSVD_ERR_UNSUPPORTED, "graph capture is for single-token decode steps (S == 1)");
+    }
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(FSVD_ERR_HIP, "hipGetDevice failed");
     hipStream_t cs;
@@ -655,7 +662,8 @@ fsvd_status_t fsvd_decoder_layer_capture(const fsvd_decoder_layer_desc* desc, fs
     hipGraph_t graph = nullptr;
     if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess)
         return fail(FSVD_ERR_CAPTURE, "hipStreamBeginCapture failed");
-    const fsvd_status_t s = enqueue_layer(desc, cs);
+    fsvd_status_t s = FSVD_OK;
+    for (int l = 0; l < n_layers && s == FSVD_OK; ++l) s = enqueue_layer(&descs[l], cs);
     const hipError_t e = hipStreamEndCapture(cs, &graph);
     if (s != FSVD_OK) {
         if (graph) (void)hipGraphDestroy(graph);

@@ -65,6 +65,7 @@ _SIGS = {
     "fsvd_decoder_layer_ws": (_sz, [C.POINTER(DecoderLayerDesc)]),
     "fsvd_decoder_layer_run": (C.c_int, [C.POINTER(DecoderLayerDesc), _vp]),
     "fsvd_decoder_layer_capture": (C.c_int, [C.POINTER(DecoderLayerDesc), C.POINTER(_vp)]),
+    "fsvd_decoder_stack_capture": (C.c_int, [C.POINTER(DecoderLayerDesc), C.c_int, C.POINTER(_vp)]),
     "fsvd_graph_replay": (C.c_int, [_vp, _vp]),
     "fsvd_graph_destroy": (C.c_int, [_vp]),
     "fsvd_poll_device_error": (C.c_int, [_vp, _vp, C.POINTER(_i32)]),
@@ -216,6 +217,14 @@ def fsvd_decoder_layer_run(desc: DecoderLayerDesc, stream=None):
 def fsvd_decoder_layer_capture(desc: DecoderLayerDesc) -> int:
     out = _vp()
     _check(lib().fsvd_decoder_layer_capture(C.byref(desc), C.byref(out)))
+    return out.value
+
+
+def fsvd_decoder_stack_capture(descs) -> int:
+    """One graph holding the decode steps of every layer descriptor in order."""
+    arr = (DecoderLayerDesc * len(descs))(*descs)
+    out = _vp()
+    _check(lib().fsvd_decoder_stack_capture(arr, len(descs), C.byref(out)))
     return out.value
 
 

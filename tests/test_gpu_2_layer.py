@@ -101,3 +101,44 @@ def test_graph_replay_equals_eager_and_oracle(cfg, B, fold):
         fsvd.fsvd_graph_destroy(g)
     with pytest.raises(fsvd.FsvdError):
         fsvd.fsvd_graph_replay(g)
+
+
+def test_stack_graph_equals_per_layer_graphs():
+    """Three layers chained (y of layer l is x of layer l+1): one whole-stack graph replay per step
+    gives the same bits as three per-layer graph replays, step after step."""
+    cfg, B, L_max, L0, N, NL = SMALL_GQA, 3, 64, 10, 4, 3
+    say("stack graph vs per-layer graphs", NL, "layers")
+    rng = np.random.default_rng(7)
+    xs = I.round_bf16(rng.standard_normal((N, B, cfg.d)))
+
+    def build():
+        lays = []
+        for l in range(NL):
+            p = I.make_decoder_layer(cfg, B=B, S=1, seed=40 + l, random_norm_weights=True)
+            kc, vc = I.make_kv_history(B, L_max, cfg.Hkv, cfg.D, L0, seed=50 + l)
+            lays.append(DeviceLayer(cfg, p, B=B, S=1, L_max=L_max, kc=kc, vc=vc, seqlens=np.full(B, L0),
+                                    advance=True, fold_norm=True))
+        for l in range(1, NL):  # chain: layer l reads layer l-1's output
+            lays[l].desc.x = lays[l - 1].y.data_ptr()
+        return lays
+
+    per, stack = build(), build()
+    graphs = [lay.capture() for lay in per]
+    sg = fsvd.fsvd_decoder_stack_capture([lay.desc for lay in stack])
+    try:
+        for t in range(N):
+            xt = to_dev(xs[t]).reshape(B, 1, cfg.d)
+            per[0].x.copy_(xt)
+            stack[0].x.copy_(xt)
+            for g in graphs:
+                fsvd.fsvd_graph_replay(g)
+            fsvd.fsvd_graph_replay(sg)
+            torch.cuda.synchronize()
+            assert np.array_equal(bits(per[-1].y), bits(stack[-1].y)), f"step {t}"
+        for a, b in zip(per, stack):
+            assert np.array_equal(bits(a.k_cache), bits(b.k_cache))
+            assert list(b.seqlens.cpu().numpy()) == [L0 + N] * B
+    finally:
+        for g in graphs:
+            fsvd.fsvd_graph_destroy(g)
+        fsvd.fsvd_graph_destroy(sg)
