@@ -50,6 +50,46 @@ __device__ __forceinline__ float row16_sum(float v) {
     v += dpp_f<0x128>(v);  // row_ror:8
     return v;
 }
+// Reduce-scatter over each 16-lane row of V (a power of two) per-lane partials.  Four pairing
+// levels, each pairing lanes that hold the same set of values and differ in one lane bit:
+// row_mirror (bit 3), row_half_mirror (bit 2), quad_perm xor 2 (bit 1), quad_perm xor 1 (bit 0).
+// At a level each lane keeps the half of its values selected by its bit and adds the partner's
+// copy of that half; once one value is left, the remaining levels add it across the pair.  On
+// return v[0 .. rs16_count<V>()) hold this lane's row sums of values rs16_first<V>(lane) + i.
+// The pairs of a level are independent, so the DPP operations pipeline instead of forming V
+// serial chains.
+template <int V>
+__host__ __device__ constexpr int rs16_count() { return V >= 16 ? V / 16 : 1; }
+template <int V>
+__device__ __forceinline__ int rs16_first(int lane) {
+    constexpr int lg = V >= 16 ? 4 : (V >= 8 ? 3 : (V >= 4 ? 2 : (V >= 2 ? 1 : 0)));
+    return ((lane & 15) >> (4 - lg)) * rs16_count<V>();
+}
+template <int CTRL, int BIT, int N>
+__device__ __forceinline__ void rs16_level(float* v, int lane) {
+    if constexpr (N >= 2) {
+        const bool up = (lane >> BIT) & 1;
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) {
+            const float lo = v[i], hi = v[i + N / 2];
+            const float keep = up ? hi : lo, send = up ? lo : hi;
+            v[i] = keep + dpp_f<CTRL>(send);
+        }
+    } else {
+        v[0] += dpp_f<CTRL>(v[0]);
+    }
+}
+template <int V>
+__device__ __forceinline__ void row16_reduce_scatter(float (&v)[V], int lane) {
+    static_assert((V & (V - 1)) == 0, "power of two");
+    constexpr int N1 = V, N2 = V >= 2 ? V / 2 : 1, N3 = V >= 4 ? V / 4 : 1, N4 = V >= 8 ? V / 8 : 1;
+    rs16_level<0x140, 3, N1>(v, lane);  // row_mirror
+    rs16_level<0x141, 2, N2>(v, lane);  // row_half_mirror
+    rs16_level<0x4E, 1, N3>(v, lane);   // quad_perm [2,3,0,1]
+    rs16_level<0xB1, 0, N4>(v, lane);   // quad_perm [1,0,3,2]
+}
+__host__ __device__ constexpr int pow2_ceil(int n) { return n <= 1 ? 1 : 2 * pow2_ceil((n + 1) / 2); }
+
 __device__ __forceinline__ float row16_max(float v) {
     v = fmaxf(v, dpp_f<0xB1>(v));
     v = fmaxf(v, dpp_f<0x4E>(v));

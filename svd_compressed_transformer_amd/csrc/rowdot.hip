@@ -252,21 +252,26 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
     for (; s0 + U <= nsteps; s0 += U) pass(std::integral_constant<int, U>(), s0);
     for (; s0 < nsteps; ++s0) pass(std::integral_constant<int, 1>(), s0);
 
-    // lanes -> 4 row partials per value (DPP), then waves/rows combined through LDS
-    constexpr int NV = (kR + 1) * BMAX;
-    __shared__ float red[kMaxWaves][4][NV];
+    // Cross-lane reduction: a reduce-scatter over each 16-lane row leaves every lane with the row
+    // sums of its own block of the wave's values (the kR x BMAX products and, in phase 1, the BMAX
+    // sums of squares); the 4 rows of a wave and the ksplit waves of a unit are summed from LDS.
+    constexpr int NV = (EPI == EPI_Z ? kR + 1 : kR) * BMAX;
+    constexpr int VP = pow2_ceil(NV);
+    float vals[VP];
 #pragma unroll
     for (int b = 0; b < BMAX; ++b) {
-        if (b >= M) continue;
 #pragma unroll
-        for (int r = 0; r < kR; ++r) {
-            const float v = row16_sum(acc[r][b]);
-            if ((lane & 15) == 0) red[wave][lane >> 4][r * BMAX + b] = v;
-        }
-        if (norm) {
-            const float v = row16_sum(ss[b]);
-            if ((lane & 15) == 0) red[wave][lane >> 4][kR * BMAX + b] = v;
-        }
+        for (int r = 0; r < kR; ++r) vals[r * BMAX + b] = acc[r][b];
+        if constexpr (EPI == EPI_Z) vals[kR * BMAX + b] = ss[b];
+    }
+#pragma unroll
+    for (int i = NV; i < VP; ++i) vals[i] = 0.f;
+    row16_reduce_scatter<VP>(vals, lane);
+    __shared__ float red[kMaxWaves][4][VP];
+    {
+        float* dst = &red[wave][lane >> 4][rs16_first<VP>(lane)];
+#pragma unroll
+        for (int i = 0; i < rs16_count<VP>(); ++i) dst[i] = vals[i];
     }
     __syncthreads();
 
@@ -277,10 +282,16 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
     // value r (row or statistic) of unit group g, wave set h, activation row b: the sum over the
     // ksplit waves of that set and their 4 DPP rows
     auto val = [&](int g, int h, int r, int b) -> float {
-        float s = 0.f;
         const int w0 = (g * NS + h) * ksplit;
-        for (int w = w0; w < w0 + ksplit; ++w)
-            s += red[w][0][r * BMAX + b] + red[w][1][r * BMAX + b] + red[w][2][r * BMAX + b] + red[w][3][r * BMAX + b];
+        const int vi = r * BMAX + b;
+        float s = 0.f;
+        // all reads issued together: waves past the group's ksplit read a valid slot, weighted 0
+#pragma unroll
+        for (int w = 0; w < kMaxWaves; ++w) {
+            const float* e = &red[min(w0 + w, kMaxWaves - 1)][0][vi];
+            const float t = (e[0] + e[VP]) + (e[2 * VP] + e[3 * VP]);
+            s += w < ksplit ? t : 0.f;
+        }
         return s;
     };
 
