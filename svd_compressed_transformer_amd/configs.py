@@ -1,0 +1,261 @@
+"""Measurements of the low-rank layer path at each configured shape, on one GPU.
+
+    python -m svd_compressed_transformer_amd.configs [--only NAME[,NAME...]]
+
+One JSON line per measurement on stdout:
+
+- linear_fp32: one fused low-rank linear in fp32, x 16 x 256, U 256 x 64, V 64 x 256 (the
+  operands stay in L2; launch-latency bound, time only).
+- bert_layer: BERT-Base-shaped post-norm encoder layer, batch 8 x 512, rank 384 on every
+  projection, composed of the entry points (Q/K/V, attention without mask, O + residual,
+  LayerNorm, GELU MLP + residual, LayerNorm), eager: layer time, the projections' TFLOP/s and
+  fraction of the bf16 MFMA peak, attention time, peak activation bytes.
+- decode_llama7b_b{1,8,16}: 4 distinct Llama-7B-shaped layers (rank 1638 on every projection),
+  history held at 2048 (no length advance): per-layer graph replay (the measured configuration),
+  one graph per decode step, and eager launches; tokens/s per layer, achieved GB/s of the
+  algorithmic bytes and their fraction of 8 TB/s.
+- decode_llama3_8b_gqa_b32: the same for 4 Llama-3-8B-shaped GQA layers (32 Q / 8 KV heads,
+  d_ff 14336, ranks q 1536, k 512, v 256, o 1024, gate 1024, up 1536, down 512), batch 32,
+  history 8192.
+
+Timing: warm-up passes, then windows of K passes with K chosen so a window lasts at least 20 ms;
+the median of 5 windows.  Factors are drawn on the device with the seeded recipe's
+distributions (U ~ N(0, 1/d_in), V ~ N(0, 1/r) diag(i^-0.5)); only timing is measured here,
+parity is the test suite's.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import statistics
+import sys
+
+import torch
+
+from svd_compressed_transformer_amd import fsvd, inputs as I
+from svd_compressed_transformer_amd.device import pack_rows_dev, pad_cols_dev
+from svd_compressed_transformer_amd.sweep import StackLayer, _factor, decode_bytes
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def timed_median(fn, stream, min_ms=20.0, windows=5, warm=3):
+    """Median over `windows` windows of K calls of fn (K so that a window lasts >= min_ms), in
+    ms per call, timed with HIP events on `stream`."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    est = max(e0.elapsed_time(e1), 1e-3)
+    K = max(1, math.ceil(min_ms / est))
+    res = []
+    for _ in range(windows):
+        e0.record(stream)
+        for _ in range(K):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) / K)
+    return statistics.median(res)
+
+
+# ----------------------------------------------------------------------------- single linear, fp32
+
+
+def run_linear_fp32(dev, stream):
+    c = I.CFG0
+    x = torch.randn((c.M, c.K), device=dev)
+    Ut = torch.randn((c.r, c.K), device=dev) / math.sqrt(c.K)
+    Vt = torch.randn((c.N, c.r), device=dev) / math.sqrt(c.r)
+    y = torch.empty((c.M, c.N), device=dev)
+    ws = fsvd.workspace(fsvd.fsvd_lowrank_linear_ws(c.M, c.K, c.r, c.N, fsvd.FSVD_F32), device=dev)
+
+    def call():
+        fsvd.fsvd_lowrank_linear(x, c.M, c.K, c.K, Ut, c.r, c.K, Vt, c.N, c.r, None, None, c.N, y, c.N,
+                                 fsvd.FSVD_F32, ws, ws.numel(), stream)
+
+    ms = timed_median(call, stream, min_ms=5.0)
+    by = 4 * (c.M * c.K + c.r * c.K + c.N * c.r + c.M * c.N)
+    return {"config": "linear_fp32", "M": c.M, "K": c.K, "rank": c.r, "N": c.N, "us_per_call": round(ms * 1e3, 2),
+            "algorithmic_bytes": by, "note": "operands resident in L2; launch-latency bound"}
+
+
+# ----------------------------------------------------------------------------- BERT-Base encoder layer
+
+
+def run_bert_layer(dev, stream):
+    cfg, B, S = I.CFG1, I.CFG1_BATCH, I.CFG1_SEQ
+    d, H, D, dff = cfg.d, cfg.H, cfg.D, cfg.d_ff
+    M = B * S
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    r = cfg.ranks
+    f = {p: _factor(gen, *dims, r[p], dev) for p, dims in (
+        ("q", (d, H * D)), ("k", (d, H * D)), ("v", (d, H * D)), ("o", (H * D, d)), ("up", (d, dff)),
+        ("down", (dff, d)))}
+    A, (rq, rk, rv) = pack_rows_dev([f["q"][0], f["k"][0], f["v"][0]], device=dev)
+    Vq, Vk, Vv = (pad_cols_dev(f["q"][1], rq, dev), pad_cols_dev(f["k"][1], rk, dev), pad_cols_dev(f["v"][1], rv, dev))
+    Uo, (ro,) = pack_rows_dev([f["o"][0]], device=dev)
+    Vo = pad_cols_dev(f["o"][1], ro, dev)
+    Uu, (ru,) = pack_rows_dev([f["up"][0]], device=dev)
+    Vu = pad_cols_dev(f["up"][1], ru, dev)
+    Ud, (rd,) = pack_rows_dev([f["down"][0]], device=dev)
+    Vd = pad_cols_dev(f["down"][1], rd, dev)
+    del f
+    g1 = torch.ones(d, dtype=torch.bfloat16, device=dev)
+    b1 = torch.zeros(d, dtype=torch.bfloat16, device=dev)
+    x = torch.randn((M, d), generator=gen, device=dev).to(torch.bfloat16)
+    torch.cuda.synchronize()
+
+    # everything the layer call allocates beyond its inputs and weights: activations + workspace
+    torch.cuda.reset_peak_memory_stats(dev)
+    base = torch.cuda.memory_allocated(dev)
+    bf = fsvd.FSVD_BF16
+    kc = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    q = torch.empty((M, H * D), dtype=torch.bfloat16, device=dev)
+    o = torch.empty_like(q)
+    h = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+    fo = torch.empty_like(h)
+    y = torch.empty_like(h)
+    sl = torch.zeros(B, dtype=torch.int32, device=dev)
+    ws = fsvd.workspace(max(fsvd.fsvd_lowrank_qkv_ws(B, S, d, rq, rk, rv, H, H, D),
+                            fsvd.fsvd_decode_attn_dense_kv_ws(B, S, H, H, D, S),
+                            fsvd.fsvd_lowrank_linear_ws(M, H * D, ro, d, bf),
+                            fsvd.fsvd_lowrank_mlp_packed_ws(M, d, 0, ru, dff, rd)), device=dev)
+    n = ws.numel()
+
+    def qkv():
+        fsvd.fsvd_lowrank_qkv(x, B, S, d, None, 0.0, A, rq, rk, rv, Vq, Vk, Vv, H, H, D, 0.0, q, kc, vc, S, sl, None,
+                              None, bf, ws, n, stream)
+
+    def attn():
+        fsvd.fsvd_decode_attn_dense_kv(q, kc, vc, S, sl, B, S, H, H, D, 0.0, 0, o, bf, ws, n, stream)
+
+    def oproj():
+        fsvd.fsvd_lowrank_linear(o, M, H * D, H * D, Uo, ro, H * D, Vo, d, ro, None, x, d, h, d, bf, ws, n, stream)
+
+    def ln1():
+        fsvd.fsvd_layernorm(h, None, g1, b1, cfg.ln_eps, M, d, h, bf, stream)
+
+    def mlp():
+        fsvd.fsvd_lowrank_mlp_packed(h, M, d, None, 0.0, fsvd.FSVD_ACT_GELU, Uu, 0, ru, None, Vu, dff, Ud, Vd, rd, h,
+                                     fo, bf, ws, n, stream)
+
+    def ln2():
+        fsvd.fsvd_layernorm(fo, None, g1, b1, cfg.ln_eps, M, d, y, bf, stream)
+
+    def layer():
+        qkv(); attn(); oproj(); ln1(); mlp(); ln2()
+
+    layer()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated(dev) - base
+    assert fsvd.fsvd_poll_device_error(ws, stream) == 0
+    t_layer = timed_median(layer, stream)
+    t_qkv, t_attn, t_o, t_mlp = (timed_median(fn, stream) for fn in (qkv, attn, oproj, mlp))
+    t_proj = t_qkv + t_o + t_mlp
+    proj_flops = 2 * M * (r["q"] * (d + H * D) + r["k"] * (d + H * D) + r["v"] * (d + H * D) + r["o"] * (H * D + d) +
+                          r["up"] * (d + dff) + r["down"] * (dff + d))
+    attn_flops = 4 * B * H * S * S * D
+    io = M * d * 2
+    unfused = 2 * io + 2 * M * dff * 2 + B * H * S * S * 4  # u and GELU(u) in bf16, fp32 scores
+    return {"config": "bert_layer", "batch": B, "seq": S, "rank": r["q"], "ms_per_layer": round(t_layer, 4),
+            "tokens_per_s_per_layer": round(M / (t_layer * 1e-3), 1),
+            "projections": {"ms": round(t_proj, 4), "qkv_ms": round(t_qkv, 4), "o_ms": round(t_o, 4),
+                            "mlp_ms": round(t_mlp, 4), "flops": int(proj_flops),
+                            "tflops": round(proj_flops / (t_proj * 1e-3) / 1e12, 1),
+                            "mfma_frac": round(proj_flops / (t_proj * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+            "attention": {"ms": round(t_attn, 4), "flops": int(attn_flops),
+                          "tflops": round(attn_flops / (t_attn * 1e-3) / 1e12, 1)},
+            "peak_activation_bytes": int(peak), "unfused_activation_bytes": int(unfused),
+            "layer_io_bytes": int(io)}
+
+
+# ----------------------------------------------------------------------------- decode stacks
+
+
+def run_decode_stack(name, cfg, ranks, B, history, layers, dev, stream):
+    L_max = history + 1
+    sl = torch.full((layers, B), history, dtype=torch.int32, device=dev)
+    ys = [torch.randn((B, 1, cfg.d), device=dev).to(torch.bfloat16) for _ in range(layers)]
+    stack = [StackLayer(cfg, ranks, B, 1, L_max, 2000 + l, dev, ys[(l - 1) % layers], ys[l], sl[l], advance=0)
+             for l in range(layers)]
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base = torch.cuda.memory_allocated(dev)
+    ws = fsvd.workspace(fsvd.fsvd_decoder_layer_ws(stack[0].desc), device=dev)
+    for lay in stack:
+        lay.desc.ws, lay.desc.ws_bytes = ws.data_ptr(), ws.numel()
+    fsvd.fsvd_decoder_layer_run(stack[0].desc, stream)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated(dev) - base
+    graphs = [fsvd.fsvd_decoder_layer_capture(lay.desc) for lay in stack]
+    sg = fsvd.fsvd_decoder_stack_capture([lay.desc for lay in stack])
+
+    def per_layer():
+        for g in graphs:
+            fsvd.fsvd_graph_replay(g, stream)
+
+    def one_graph():
+        fsvd.fsvd_graph_replay(sg, stream)
+
+    def eager():
+        for lay in stack:
+            fsvd.fsvd_decoder_layer_run(lay.desc, stream)
+
+    us = {k: timed_median(fn, stream) * 1e3 / layers for k, fn in
+          (("per_layer_graphs", per_layer), ("one_graph_per_step", one_graph), ("eager", eager))}
+    assert fsvd.fsvd_poll_device_error(ws, stream) == 0
+    for g in graphs:
+        fsvd.fsvd_graph_destroy(g)
+    fsvd.fsvd_graph_destroy(sg)
+    by = decode_bytes(cfg, ranks, B, history + 1)
+    u = us["per_layer_graphs"]
+    res = {"config": name, "batch": B, "history": history, "layers": layers, "ranks": ranks,
+           "us_per_layer_step": round(u, 2), "tokens_per_s_per_layer": round(B / (u * 1e-6), 1),
+           "algorithmic_bytes": int(by), "achieved_gbs": round(by / (u * 1e-6) / 1e9, 1),
+           "hbm_frac": round(by / (u * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "comparators_us_per_layer_step": {k: round(v, 2) for k, v in us.items() if k != "per_layer_graphs"},
+           "peak_activation_bytes": int(peak)}
+    del stack, graphs, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--only", default="", help="comma-separated subset of the measurement names")
+    args = ap.parse_args()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.set_stream(stream)
+    runs = [("linear_fp32", lambda: run_linear_fp32(dev, stream)),
+            ("bert_layer", lambda: run_bert_layer(dev, stream))]
+    for B in I.CFG2_BATCHES:
+        runs.append((f"decode_llama7b_b{B}",
+                     lambda B=B: run_decode_stack(f"decode_llama7b_b{B}", I.CFG2, dict(I.CFG2.ranks), B,
+                                                  I.CFG2_KV_LEN, 4, dev, stream)))
+    runs.append(("decode_llama3_8b_gqa_b32",
+                 lambda: run_decode_stack("decode_llama3_8b_gqa_b32", I.CFG4, dict(I.CFG4.ranks), I.CFG4_BATCH,
+                                          I.CFG4_KV_LEN, 4, dev, stream)))
+    only = set(filter(None, args.only.split(",")))
+    for name, fn in runs:
+        if only and name not in only:
+            continue
+        log(name, "...")
+        print(json.dumps(fn()), flush=True)
+
+
+if __name__ == "__main__":
+    main()

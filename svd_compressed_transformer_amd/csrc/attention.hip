@@ -24,6 +24,15 @@ constexpr float kNegBig = -1.0e30f;
 #ifndef FSVD_ATTN_WGS
 #define FSVD_ATTN_WGS 4096  // decode: target workgroups (sequence x kv head x length partition)
 #endif
+#ifndef FSVD_ATTN_NP
+#define FSVD_ATTN_NP 2      // decode: positions per lane group per iteration (16 * NP per workgroup)
+#endif
+#ifndef FSVD_ATTN_ROUND
+#define FSVD_ATTN_ROUND 16  // decode: partition lengths are multiples of this
+#endif
+#ifndef FSVD_ATTN_MERGE_C
+#define FSVD_ATTN_MERGE_C 32  // partition merge: partitions loaded per round trip
+#endif
 
 // EPL: head elements per lane (D / 16): 8 for D = 128, 4 for D = 64.  G: query heads per kv head.
 template <int EPL>
@@ -58,7 +67,7 @@ __global__ __launch_bounds__(256) void attn_decode_split(const AttnArgs a) {
         if (tid == 0 && split == 0) set_dev_error(a.err, FSVD_DEVERR_SEQ_OVERFLOW);
         n = a.L_max;
     }
-    const int64_t chunk = ((n + a.nsplit - 1) / a.nsplit + 15) / 16 * 16;
+    const int64_t chunk = ((n + a.nsplit - 1) / a.nsplit + FSVD_ATTN_ROUND - 1) / FSVD_ATTN_ROUND * FSVD_ATTN_ROUND;
     const int64_t j0 = (int64_t)split * chunk;
     const int64_t j1 = min(n, j0 + chunk);
 
@@ -90,7 +99,7 @@ __global__ __launch_bounds__(256) void attn_decode_split(const AttnArgs a) {
     // current ones are used (two iterations in flight per wave); loads are unconditional, rows past
     // the partition re-read its first row, and such positions get zero weight.  The running max
     // is updated once per iteration for all NP positions, so the rescale of l and o is paid once.
-    constexpr int NP = 2;
+    constexpr int NP = FSVD_ATTN_NP;
     KV<EPL> kv[NP], vv[NP];
     auto load = [&](int64_t jb, KV<EPL> (&kk)[NP], KV<EPL> (&vk)[NP]) {
 #pragma unroll
@@ -194,7 +203,7 @@ __global__ __launch_bounds__(128) void attn_decode_combine(const AttnArgs a) {
     const int t = threadIdx.x;
     if (t >= D) return;
     const float* part = a.part + (int64_t)bh * ns * (D + 2);
-    constexpr int C = 16;
+    constexpr int C = FSVD_ATTN_MERGE_C;
     float M = kNegBig, L = 0.f, O = 0.f;
     for (int s0 = 0; s0 < ns; s0 += C) {
         float ms[C], ls[C], os[C];

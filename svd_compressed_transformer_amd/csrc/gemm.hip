@@ -3,11 +3,12 @@
 // At prefill the two phases of y = (x . U) . V are dense contractions with M = B*S in the
 // thousands (about M flop per factor byte, far above the MFMA ridge), so each phase runs as an
 // NT GEMM C[M, N] = A[M, K] . B[N, K]^T on the matrix cores with a fused epilogue:
-//   - tiles of BM x BN (256 or 128 x 256 or 128), four waves as 2 x 2, each wave a grid of
-//     32 x 32 blocks computed with v_mfma_f32_32x32x16_bf16 (fp32 accumulation);
+//   - tiles of BM x BN (256 x 256 down to 64 x 128, the largest that still fills the chip), four
+//     waves as 2 x 2, each wave a grid of 32 x 32 blocks computed with
+//     v_mfma_f32_32x32x16_bf16 (fp32 accumulation);
 //   - operands move global -> LDS directly (global_load_lds_dwordx4, no staging registers) through
-//     a 2- or 3-stage pipeline of BK = 64 slices (one whole 128-byte line per row and stage, which
-//     the load path serves about 1.4x faster than half lines), each lane choosing the global chunk
+//     a 3- or 4-stage pipeline of BK = 64 or 32 slices (BK = 64: one whole 128-byte line per row
+//     and stage), each lane choosing the global chunk
 //     whose XOR-swizzled LDS home is its slot, so the fragment reads of one MFMA hit distinct
 //     banks; M/N tails re-read the last row (never stored), the K tail is zeroed in LDS;
 //   - tiles are handed out XCD by XCD (workgroup i runs on XCD i mod 8) so the WGs that share an
@@ -31,9 +32,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kThreads = 256;   // 4 waves, arranged 2 x 2
 
 // Per tile shape: k per LDS stage (KB) and pipeline depth.  256 x 256 tiles stage BK = 32 slices
-// four deep (4 x 32 KiB); 128 x 256 and 256 x 128 tiles stage BK = 64 slices, one whole 128-byte
-// line per row (the load path serves whole lines about 1.4x faster than half lines), three deep
-// (3 x 48 KiB).  Measured on MI355X, the deeper pipeline matters more for the big tile.
+// four deep (4 x 32 KiB); the smaller tiles (128 x 256, 256 x 128, 128 x 128, 64 x 128) stage
+// BK = 64 slices, one whole 128-byte line per row (the load path serves whole lines about 1.4x
+// faster than half lines), three deep (3 x 48 KiB for 128 x 256).  Measured on MI355X, the deeper
+// pipeline matters more for the big tile.
 template <int BM, int BN>
 constexpr int kb_for() { return BM + BN > 384 ? 32 : 64; }
 template <int BM, int BN>
@@ -493,24 +495,35 @@ fsvd_status_t launch_t(const GemmArgs& g, hipStream_t st) {
     return check_launch("gemm");
 }
 
+// Tile choice: the largest tile whose grid still covers the 256 CUs (256 x 256 only with at least
+// two workgroups per CU), down to 64 x 128 for small M x N, where a big tile would leave most CUs
+// idle.  The Q/K/V epilogue rotates RoPE pairs (c, c + D/2) inside one wave tile, so with D = 128
+// it needs the 128-wide wave tiles of BN = 256.
+template <int EPI>
+fsvd_status_t launch_epi(const GemmArgs& g, hipStream_t st) {
+    auto tiles = [&](int bm, int bn) { return ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn); };
+    if constexpr (EPI == GEPI_SWIGLU) {
+        if (tiles(256, 128) >= 256) return launch_t<256, 128, EPI>(g, st);
+    } else {
+        if (tiles(256, 256) >= 512) return launch_t<256, 256, EPI>(g, st);
+        if (tiles(128, 256) >= 256 || (EPI == GEPI_QKV && g.D > 64)) return launch_t<128, 256, EPI>(g, st);
+    }
+    if (tiles(128, 128) >= 256) return launch_t<128, 128, EPI>(g, st);
+    return launch_t<64, 128, EPI>(g, st);
+}
+
 }  // namespace
 
 fsvd_status_t launch_gemm(const GemmArgs& g, int epi, hipStream_t st) {
     if (g.M <= 0 || g.N <= 0) return FSVD_OK;
     if (g.K <= 0 || (epi == GEPI_SWIGLU && g.K2 <= 0)) return fail(FSVD_ERR_INVALID_ARG, "gemm: empty reduction");
     if (epi == GEPI_QKV && (g.D != 64 && g.D != 128)) return fail(FSVD_ERR_UNSUPPORTED, "RoPE epilogue needs D in {64,128}");
-    // tile choice: 256 x 256 when the grid still covers the chip, else 128 x 256
-    const int t256 = ((g.M + 255) / 256) * ((g.N + 255) / 256);
     switch (epi) {
-        case GEPI_STORE:
-            return t256 >= 512 ? launch_t<256, 256, GEPI_STORE>(g, st) : launch_t<128, 256, GEPI_STORE>(g, st);
-        case GEPI_LINEAR:
-            return t256 >= 512 ? launch_t<256, 256, GEPI_LINEAR>(g, st) : launch_t<128, 256, GEPI_LINEAR>(g, st);
-        case GEPI_QKV:
-            return t256 >= 512 ? launch_t<256, 256, GEPI_QKV>(g, st) : launch_t<128, 256, GEPI_QKV>(g, st);
-        case GEPI_SWIGLU: return launch_t<256, 128, GEPI_SWIGLU>(g, st);
-        case GEPI_GELU:
-            return t256 >= 512 ? launch_t<256, 256, GEPI_GELU>(g, st) : launch_t<128, 256, GEPI_GELU>(g, st);
+        case GEPI_STORE: return launch_epi<GEPI_STORE>(g, st);
+        case GEPI_LINEAR: return launch_epi<GEPI_LINEAR>(g, st);
+        case GEPI_QKV: return launch_epi<GEPI_QKV>(g, st);
+        case GEPI_SWIGLU: return launch_epi<GEPI_SWIGLU>(g, st);
+        case GEPI_GELU: return launch_epi<GEPI_GELU>(g, st);
     }
     return fail(FSVD_ERR_UNSUPPORTED, "unknown gemm epilogue %d", epi);
 }

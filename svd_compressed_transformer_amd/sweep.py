@@ -19,7 +19,7 @@ import sys
 
 import torch
 
-from svd_compressed_transformer_amd import fsvd
+from svd_compressed_transformer_amd import fsvd, inputs as I
 from svd_compressed_transformer_amd.device import pack_rows_dev, pad_cols_dev
 
 D_MODEL, HEADS, HEAD_DIM, D_FF = 4096, 32, 128, 11008
@@ -39,19 +39,20 @@ def _factor(gen, d_in, d_out, r, dev):
 
 
 class StackLayer:
-    """One decoder layer's packed factors and KV cache on the device, and its descriptor."""
+    """One decoder layer's packed factors and KV cache on the device, and its descriptor.
 
-    def __init__(self, B, S, L_max, ratio, seed, dev, kv_history, x, y, seqlens):
+    cfg gives the layer shape (hidden, heads, head dim, d_ff, norm eps, RoPE theta); ranks maps
+    each projection (q, k, v, o, gate, up, down) to its logical rank."""
+
+    def __init__(self, cfg, ranks, B, S, L_max, seed, dev, x, y, seqlens, advance=1):
         gen = torch.Generator(device=dev)
         gen.manual_seed(seed)
-        r = int(math.floor(ratio * min(D_MODEL, D_MODEL) + 1e-9))
-        r_ff = int(math.floor(ratio * min(D_MODEL, D_FF) + 1e-9))
-        f = {p: _factor(gen, *dims, dev) for p, dims in (
-            ("q", (D_MODEL, HEADS * HEAD_DIM, r)), ("k", (D_MODEL, HEADS * HEAD_DIM, r)),
-            ("v", (D_MODEL, HEADS * HEAD_DIM, r)), ("o", (HEADS * HEAD_DIM, D_MODEL, r)),
-            ("gate", (D_MODEL, D_FF, r_ff)), ("up", (D_MODEL, D_FF, r_ff)), ("down", (D_FF, D_MODEL, r_ff)))}
-        self.attn_w = (1.0 + 0.1 * torch.randn(D_MODEL, generator=gen, device=dev)).to(torch.bfloat16)
-        self.mlp_w = (1.0 + 0.1 * torch.randn(D_MODEL, generator=gen, device=dev)).to(torch.bfloat16)
+        d, qd, kd = cfg.d, cfg.Hq * cfg.D, cfg.Hkv * cfg.D
+        dims = {"q": (d, qd), "k": (d, kd), "v": (d, kd), "o": (qd, d), "gate": (d, cfg.d_ff), "up": (d, cfg.d_ff),
+                "down": (cfg.d_ff, d)}
+        f = {p: _factor(gen, *dims[p], ranks[p], dev) for p in dims}
+        self.attn_w = (1.0 + 0.1 * torch.randn(d, generator=gen, device=dev)).to(torch.bfloat16)
+        self.mlp_w = (1.0 + 0.1 * torch.randn(d, generator=gen, device=dev)).to(torch.bfloat16)
         self.A_qkv, (rq, rk, rv) = pack_rows_dev([f["q"][0], f["k"][0], f["v"][0]], device=dev, col_scale=self.attn_w)
         self.Vq, self.Vk, self.Vv = (pad_cols_dev(f["q"][1], rq, dev), pad_cols_dev(f["k"][1], rk, dev),
                                      pad_cols_dev(f["v"][1], rv, dev))
@@ -62,24 +63,33 @@ class StackLayer:
         self.Ud, (rd,) = pack_rows_dev([f["down"][0]], device=dev)
         self.Vd = pad_cols_dev(f["down"][1], rd, dev)
         del f
-        self.logical = dict(q=r, k=r, v=r, o=r, gate=r_ff, up=r_ff, down=r_ff)
-        shape = (B, L_max, HEADS, HEAD_DIM)
+        self.logical = dict(ranks)
+        shape = (B, L_max, cfg.Hkv, cfg.D)
         self.kc = torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
         self.vc = torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
         self.desc = fsvd.decoder_layer_desc(
-            B=B, S=S, d=D_MODEL, Hq=HEADS, Hkv=HEADS, D=HEAD_DIM, d_ff=D_FF, L_max=L_max, r_q=rq, r_k=rk, r_v=rv,
-            r_o=ro, r_g=rg, r_u=ru, r_d=rd, norm_eps=1e-6, rope_theta=1e4, softmax_scale=0.0, advance_seqlens=1,
-            flags=fsvd.FSVD_LAYER_NORM_FOLDED, x=x, y=y, attn_norm_w=None, mlp_norm_w=None, A_qkv=self.A_qkv,
-            Vt_q=self.Vq, Vt_k=self.Vk, Vt_v=self.Vv, Ut_o=self.Uo, Vt_o=self.Vo, A_gu=self.A_gu, Vt_g=self.Vg,
-            Vt_u=self.Vu, Ut_d=self.Ud, Vt_d=self.Vd, k_cache=self.kc, v_cache=self.vc, cache_seqlens=seqlens)
+            B=B, S=S, d=d, Hq=cfg.Hq, Hkv=cfg.Hkv, D=cfg.D, d_ff=cfg.d_ff, L_max=L_max, r_q=rq, r_k=rk, r_v=rv,
+            r_o=ro, r_g=rg, r_u=ru, r_d=rd, norm_eps=cfg.norm_eps, rope_theta=cfg.rope_theta, softmax_scale=0.0,
+            advance_seqlens=advance, flags=fsvd.FSVD_LAYER_NORM_FOLDED, x=x, y=y, attn_norm_w=None, mlp_norm_w=None,
+            A_qkv=self.A_qkv, Vt_q=self.Vq, Vt_k=self.Vk, Vt_v=self.Vv, Ut_o=self.Uo, Vt_o=self.Vo, A_gu=self.A_gu,
+            Vt_g=self.Vg, Vt_u=self.Vu, Ut_d=self.Ud, Vt_d=self.Vd, k_cache=self.kc, v_cache=self.vc,
+            cache_seqlens=seqlens)
 
 
-def decode_bytes(logical, B, L_read):
-    """Algorithmic HBM bytes of one decode layer-step (factors once, KV read once, new K/V, I/O)."""
-    d, qd = D_MODEL, HEADS * HEAD_DIM
+def uniform_ranks(ratio):
+    """Llama-7B-shaped layer: every projection at rank floor(ratio * 4096)."""
+    r = int(math.floor(ratio * D_MODEL + 1e-9))
+    return dict(q=r, k=r, v=r, o=r, gate=r, up=r, down=r)
+
+
+def decode_bytes(cfg, logical, B, L_read):
+    """Algorithmic HBM bytes of one decode layer-step: every factor byte once (logical ranks), the
+    KV cache read once over L_read positions, the new K/V written, the layer input and output."""
+    d, qd, kd = cfg.d, cfg.Hq * cfg.D, cfg.Hkv * cfg.D
     r = logical
-    fac = 2 * (r["q"] * (d + qd) * 3 + r["o"] * (qd + d) + r["gate"] * (d + D_FF) * 2 + r["down"] * (D_FF + d))
-    return fac + 2 * 2 * B * L_read * qd + 2 * 2 * B * qd + 2 * 2 * B * d
+    fac = 2 * (r["q"] * (d + qd) + r["k"] * (d + kd) + r["v"] * (d + kd) + r["o"] * (qd + d) +
+               r["gate"] * (d + cfg.d_ff) + r["up"] * (d + cfg.d_ff) + r["down"] * (cfg.d_ff + d))
+    return fac + 2 * 2 * B * L_read * kd + 2 * 2 * B * kd + 2 * 2 * B * d
 
 
 def run_decode(B, history, ratio, layers, steps, dev, stream, one_graph=True):
@@ -88,7 +98,8 @@ def run_decode(B, history, ratio, layers, steps, dev, stream, one_graph=True):
     ys = [torch.randn((B, 1, D_MODEL), device=dev).to(torch.bfloat16) for _ in range(layers)]
     stack = []
     for l in range(layers):
-        stack.append(StackLayer(B, 1, L_max, ratio, 1000 + l, dev, history, ys[(l - 1) % layers], ys[l], sl[l]))
+        stack.append(StackLayer(I.CFG2, uniform_ranks(ratio), B, 1, L_max, 1000 + l, dev, ys[(l - 1) % layers], ys[l],
+                                sl[l]))
     ws = fsvd.workspace(fsvd.fsvd_decoder_layer_ws(stack[0].desc), device=dev)
     for lay in stack:
         lay.desc.ws, lay.desc.ws_bytes = ws.data_ptr(), ws.numel()
@@ -115,7 +126,7 @@ def run_decode(B, history, ratio, layers, steps, dev, stream, one_graph=True):
         fsvd.fsvd_graph_destroy(g)
     if sg:
         fsvd.fsvd_graph_destroy(sg)
-    by = decode_bytes(stack[0].logical, B, history + 1 + steps // 2)
+    by = decode_bytes(I.CFG2, stack[0].logical, B, history + 1 + steps // 2)
     res = {"sweep": "decode", "batch": B, "history": history, "rank_ratio": ratio, "layers": layers,
            "rank": stack[0].logical["q"], "us_per_layer_step": round(us, 2),
            "tokens_per_s_per_layer": round(B / (us * 1e-6), 1), "algorithmic_bytes": int(by),
@@ -132,8 +143,7 @@ def run_prefill(B, S, ratio, dev, stream, reps=3):
     sl = torch.zeros((1, B), dtype=torch.int32, device=dev)
     x = torch.randn((B, S, D_MODEL), device=dev).to(torch.bfloat16)
     y = torch.empty_like(x)
-    lay = StackLayer(B, S, L_max, ratio, 7, dev, 0, x, y, sl[0])
-    lay.desc.advance_seqlens = 0
+    lay = StackLayer(I.CFG2, uniform_ranks(ratio), B, S, L_max, 7, dev, x, y, sl[0], advance=0)
     ws = fsvd.workspace(fsvd.fsvd_decoder_layer_ws(lay.desc), device=dev)
     lay.desc.ws, lay.desc.ws_bytes = ws.data_ptr(), ws.numel()
     fsvd.fsvd_decoder_layer_run(lay.desc, stream)
