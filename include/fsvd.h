@@ -11,8 +11,11 @@
  *   [V1]    "FlashSVD: Memory-Efficient Inference with Streaming for Low-Rank Models", abstract:
  *           fused low-rank projections in attention and FFN; factor tiles streamed through
  *           on-chip memory so full-size activation buffers are never materialised.
- *   [V15-M1] "FlashSVD v1.5: Making Low-Rank Transformers Inference Actually Fast" (explainer),
- *           Methodology 1, Unified Runtime Abstraction: one common factorized representation.
+ *   [V15-PS] "FlashSVD v1.5: Making Low-Rank Transformers Inference Actually Fast" (explainer),
+ *           Problem Statement: rebuilding the attention history from the factors at every step
+ *           means irregular access and recomputation.
+ *   [V15-M1] same page, Methodology 1, Unified Runtime Abstraction: one common factorized
+ *           representation.
  *   [V15-M2] same page, Methodology 2, Dense-KV Attention: rebuild dense Q/K/V for the current
  *           tokens only, keep history in a contiguous dense KV cache read in one attention step.
  *   [V15-M3] same page, Methodology 3, Packed MLP Execution: gate and up input-side factors
@@ -63,7 +66,7 @@ extern "C" {
 
 typedef struct ihipStream_t* fsvd_stream_t; /* a hipStream_t */
 
-#define FSVD_ABI_VERSION 2
+#define FSVD_ABI_VERSION 3
 
 typedef enum {
     FSVD_OK = 0,
@@ -194,6 +197,29 @@ fsvd_status_t fsvd_decode_attn_dense_kv(const void* q, const void* k_cache, cons
                                         const int32_t* cache_seqlens, int64_t B, int64_t Sq, int64_t Hq,
                                         int64_t Hkv, int64_t D, float softmax_scale, int causal, void* out,
                                         fsvd_dtype_t dtype, void* ws, size_t ws_bytes, fsvd_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Comparator: attention over a low-rank history  [V15-PS] [V15-M2]
+ * The layout the dense cache replaces: the history keeps only the rank-r projections of each
+ * token, z_k = a . Ut_k^T and z_v = a . Ut_v^T, and every step rebuilds the whole K and V
+ * from them before attending:
+ *   K[b, p] = RoPE(z_k[b, p] . Vt_k^T, position p),  V[b, p] = z_v[b, p] . Vt_v^T
+ * for every cached position p < L_max, then the attention of fsvd_decode_attn_dense_kv over
+ * (K, V) with the same q, cache_seqlens, scale and causal arguments.  The result equals the
+ * dense-KV path's whenever the dense cache holds RoPE(z_k . Vt_k^T) and z_v . Vt_v^T; the
+ * cost is the rebuild, a (B * L_max) x r x (Hkv * D) contraction per cache every step.
+ * zk_cache, zv_cache [B, L_max, ldz] bf16 (rows of r_k resp. r_v used; the caller appends
+ * the new tokens' z rows before the call); Vt_k [Hkv*D, r_k], Vt_v [Hkv*D, r_v] (stored,
+ * padded ranks, multiples of 8); q, out [B, Sq, Hq, D].  rope_theta 0 -> no RoPE.  The
+ * rebuilt K and V live in the workspace (2 * B * L_max * Hkv * D bf16).  bf16 only.
+ * ------------------------------------------------------------------------------------------ */
+size_t fsvd_decode_attn_lowrank_kv_ws(int64_t B, int64_t Sq, int64_t Hq, int64_t Hkv, int64_t D, int64_t L_max);
+fsvd_status_t fsvd_decode_attn_lowrank_kv(const void* q, const void* zk_cache, const void* zv_cache, int64_t ldz,
+                                          const void* Vt_k, int64_t r_k, const void* Vt_v, int64_t r_v,
+                                          int64_t L_max, const int32_t* cache_seqlens, int64_t B, int64_t Sq,
+                                          int64_t Hq, int64_t Hkv, int64_t D, float rope_theta,
+                                          float softmax_scale, int causal, void* out, fsvd_dtype_t dtype,
+                                          void* ws, size_t ws_bytes, fsvd_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * a7. Layer glue: y = LayerNorm(x + residual) * gamma + beta over rows of width d (BERT

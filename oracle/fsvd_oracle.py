@@ -170,6 +170,23 @@ def qkv_packed(x, norm_w, norm_eps, A_qkv, r_q, r_k, r_v, Vt_q, Vt_k, Vt_v, Hq, 
                Vt_v, Hq, Hkv, D, rope_theta, k_cache, v_cache, cache_seqlens)
 
 
+def lowrank_history_kv(zk, zv, Vt_k, Vt_v, Hkv, D, rope_theta):
+    """K and V of every cached position rebuilt from a rank-r history.
+
+    [V15] Problem Statement: the layout that dense-KV decoding replaces keeps only the rank-r
+    projections of past tokens, z_k = a . U_k and z_v = a . U_v, and reconstructs K and V from
+    the factors at every step.  zk [B, L, r_k], zv [B, L, r_v] (position p of a sequence at row
+    p); K rows are rotated by RoPE at their position.  Returns K, V [B, L, Hkv, D].
+    """
+    zk, zv = _a(zk), _a(zv)
+    B, L, _ = zk.shape
+    k = (zk @ _a(Vt_k).T).reshape(B, L, Hkv, D)
+    v = (zv @ _a(Vt_v).T).reshape(B, L, Hkv, D)
+    if rope_theta:
+        k = rope(k, np.arange(L)[None, :, None], rope_theta)
+    return k, v
+
+
 # ----------------------------------------------------------------------------- MLP
 
 

@@ -17,6 +17,10 @@ One JSON line per measurement on stdout:
 - decode_llama3_8b_gqa_b32: the same for 4 Llama-3-8B-shaped GQA layers (32 Q / 8 KV heads,
   d_ff 14336, ranks q 1536, k 512, v 256, o 1024, gate 1024, up 1536, down 512), batch 32,
   history 8192.
+- attn_lowrank_history_llama7b_b{1,4}: the decode attention of a Llama-7B-shaped layer over a
+  2048-token history, from the dense KV cache against the layout the dense cache replaces
+  (rank-1638 rows z_k, z_v cached per token, K and V rebuilt from them every step, then the same
+  attention); 4 distinct caches rotated.
 
 Timing: warm-up passes, then windows of K passes with K chosen so a window lasts at least 20 ms;
 the median of 5 windows.  Factors are drawn on the device with the seeded recipe's
@@ -233,6 +237,62 @@ def run_decode_stack(name, cfg, ranks, B, history, layers, dev, stream):
     return res
 
 
+# ----------------------------------------------------------------------------- dense KV vs low-rank history
+
+
+def run_attn_history(B, history, dev, stream, copies=4):
+    cfg = I.CFG2
+    Hq, Hkv, D = cfg.Hq, cfg.Hkv, cfg.D
+    r = 1640  # rank 1638 stored padded to a multiple of 8
+    L_max = history + 1
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    bf = torch.bfloat16
+    sets = []
+    for _ in range(copies):
+        sets.append(dict(
+            kc=torch.randn((B, L_max, Hkv, D), generator=gen, device=dev).to(bf),
+            vc=torch.randn((B, L_max, Hkv, D), generator=gen, device=dev).to(bf),
+            zk=torch.randn((B, L_max, r), generator=gen, device=dev).to(bf),
+            zv=torch.randn((B, L_max, r), generator=gen, device=dev).to(bf),
+            Vk=(torch.randn((Hkv * D, r), generator=gen, device=dev) / math.sqrt(r)).to(bf),
+            Vv=(torch.randn((Hkv * D, r), generator=gen, device=dev) / math.sqrt(r)).to(bf)))
+    q = torch.randn((B, 1, Hq, D), generator=gen, device=dev).to(bf)
+    out = torch.empty_like(q)
+    sl = torch.full((B,), history, dtype=torch.int32, device=dev)
+    ws_d = fsvd.workspace(fsvd.fsvd_decode_attn_dense_kv_ws(B, 1, Hq, Hkv, D, L_max), device=dev)
+    ws_l = fsvd.workspace(fsvd.fsvd_decode_attn_lowrank_kv_ws(B, 1, Hq, Hkv, D, L_max), device=dev)
+    it = {"d": 0, "l": 0}
+
+    def dense():
+        c = sets[it["d"] % copies]
+        it["d"] += 1
+        fsvd.fsvd_decode_attn_dense_kv(q, c["kc"], c["vc"], L_max, sl, B, 1, Hq, Hkv, D, 0.0, 1, out, fsvd.FSVD_BF16,
+                                       ws_d, ws_d.numel(), stream)
+
+    def lowrank():
+        c = sets[it["l"] % copies]
+        it["l"] += 1
+        fsvd.fsvd_decode_attn_lowrank_kv(q, c["zk"], c["zv"], r, c["Vk"], r, c["Vv"], r, L_max, sl, B, 1, Hq, Hkv, D,
+                                         cfg.rope_theta, 0.0, 1, out, fsvd.FSVD_BF16, ws_l, ws_l.numel(), stream)
+
+    t_d = timed_median(dense, stream) * 1e3
+    t_l = timed_median(lowrank, stream) * 1e3
+    assert fsvd.fsvd_poll_device_error(ws_l, stream) == 0
+    kv_bytes = 2 * 2 * B * L_max * Hkv * D
+    z_bytes = 2 * 2 * B * L_max * 1638
+    rebuild_flops = 2 * B * L_max * 2 * 1638 * Hkv * D
+    res = {"config": f"attn_lowrank_history_llama7b_b{B}", "batch": B, "history": history, "rank": 1638,
+           "dense_kv_us": round(t_d, 2), "lowrank_history_us": round(t_l, 2), "slowdown": round(t_l / t_d, 2),
+           "dense_kv_bytes": int(kv_bytes), "lowrank_history_bytes": int(z_bytes),
+           "rebuild_flops": int(rebuild_flops),
+           "rebuild_tflops": round(rebuild_flops / ((t_l - t_d) * 1e-6) / 1e12, 1) if t_l > t_d else None,
+           "lowrank_workspace_bytes": int(ws_l.numel())}
+    del sets, ws_l, ws_d
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--only", default="", help="comma-separated subset of the measurement names")
@@ -249,6 +309,8 @@ def main():
     runs.append(("decode_llama3_8b_gqa_b32",
                  lambda: run_decode_stack("decode_llama3_8b_gqa_b32", I.CFG4, dict(I.CFG4.ranks), I.CFG4_BATCH,
                                           I.CFG4_KV_LEN, 4, dev, stream)))
+    for B in (1, 4):
+        runs.append((f"attn_lowrank_history_llama7b_b{B}", lambda B=B: run_attn_history(B, 2048, dev, stream)))
     only = set(filter(None, args.only.split(",")))
     for name, fn in runs:
         if only and name not in only:

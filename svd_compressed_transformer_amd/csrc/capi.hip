@@ -609,6 +609,59 @@ fsvd_status_t fsvd_decode_attn_dense_kv(const void* q, const void* k_cache, cons
                         softmax_scale, causal, out, part, ns, (int*)ws, (hipStream_t)stream);
 }
 
+size_t fsvd_decode_attn_lowrank_kv_ws(int64_t B, int64_t Sq, int64_t Hq, int64_t Hkv, int64_t D, int64_t L_max) {
+    if (B <= 0 || Hkv <= 0 || D <= 0 || L_max <= 0) return kWsHeader;
+    const size_t cache = align256((size_t)B * L_max * Hkv * D * 2);
+    return fsvd_decode_attn_dense_kv_ws(B, Sq, Hq, Hkv, D, L_max) + 2 * cache;
+}
+
+fsvd_status_t fsvd_decode_attn_lowrank_kv(const void* q, const void* zk_cache, const void* zv_cache, int64_t ldz,
+                                          const void* Vt_k, int64_t r_k, const void* Vt_v, int64_t r_v,
+                                          int64_t L_max, const int32_t* cache_seqlens, int64_t B, int64_t Sq,
+                                          int64_t Hq, int64_t Hkv, int64_t D, float rope_theta,
+                                          float softmax_scale, int causal, void* out, fsvd_dtype_t dtype,
+                                          void* ws, size_t ws_bytes, fsvd_stream_t stream) {
+    TRY(need_dtype(dtype, false));
+    TRY(need_dim(B, "B")); TRY(need_dim(Sq, "Sq")); TRY(need_dim(Hq, "Hq")); TRY(need_dim(Hkv, "Hkv"));
+    TRY(need_dim(D, "D")); TRY(need_dim(L_max, "L_max")); TRY(need_dim(r_k, "r_k")); TRY(need_dim(r_v, "r_v"));
+    TRY(check_attn_shape(Hq, Hkv, D));
+    TRY(need_vec(r_k, dtype, "r_k")); TRY(need_vec(r_v, dtype, "r_v"));
+    TRY(need_ld(ldz, r_k > r_v ? r_k : r_v, dtype, "ldz"));
+    if (B * L_max > (int64_t)1 << 30) return fail(FSVD_ERR_UNSUPPORTED, "B * L_max too large");
+    TRY(need_ptr(q, "q")); TRY(need_ptr(zk_cache, "zk_cache")); TRY(need_ptr(zv_cache, "zv_cache"));
+    TRY(need_ptr(Vt_k, "Vt_k")); TRY(need_ptr(Vt_v, "Vt_v")); TRY(need_ptr(out, "out")); TRY(need_ptr(ws, "ws"));
+    if (!cache_seqlens) return fail(FSVD_ERR_INVALID_ARG, "cache_seqlens is NULL");
+    if (softmax_scale < 0.f) return fail(FSVD_ERR_INVALID_ARG, "softmax_scale must be >= 0");
+    if (rope_theta < 0.f) return fail(FSVD_ERR_INVALID_ARG, "rope_theta must be >= 0");
+    const size_t need = fsvd_decode_attn_lowrank_kv_ws(B, Sq, Hq, Hkv, D, L_max);
+    if (ws_bytes < need) return fail(FSVD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+    const int ns = attn_default_splits((int)B, (int)Hkv, L_max);
+    Carve c(ws);
+    float* part = (float*)c.take(attn_decode_ws_bytes((int)B, (int)Hq, (int)D, ns));
+    const size_t cache = (size_t)B * L_max * Hkv * D * 2;
+    bf16_t* kc = (bf16_t*)c.take(cache);
+    bf16_t* vc = (bf16_t*)c.take(cache);
+    hipStream_t st = (hipStream_t)stream;
+    // rebuild every cached position: rows (b, p) of the z caches are one M = B * L_max product
+    // each; the Q/K/V epilogue (no offsets: position = p) rotates K and writes the dense rows
+    const void* Zs[2] = {zk_cache, zv_cache};
+    const void* Vs[2] = {Vt_k, Vt_v};
+    const int64_t rs[2] = {r_k, r_v};
+    for (int i = 0; i < 2; ++i) {
+        GemmArgs h{};
+        h.A = (const bf16_t*)Zs[i]; h.lda = ldz;
+        h.Bm = (const bf16_t*)Vs[i]; h.ldb = rs[i];
+        h.M = (int)(B * L_max); h.N = (int)(Hkv * D); h.K = (int)rs[i];
+        h.S = (int)L_max; h.Hq = (int)Hq; h.Hkv = (int)Hkv; h.D = (int)D; h.rope_theta = rope_theta;
+        h.L_max = L_max; h.seqlens = nullptr; h.k_cache = kc; h.v_cache = vc;
+        h.seg = i + 1;
+        h.err = (int*)ws;
+        TRY(launch_gemm(h, GEPI_QKV, st));
+    }
+    return enqueue_attn(q, kc, vc, L_max, cache_seqlens, (int)B, (int)Sq, (int)Hq, (int)Hkv, (int)D, softmax_scale,
+                        causal, out, part, ns, (int*)ws, st);
+}
+
 fsvd_status_t fsvd_layernorm(const void* x, const void* residual, const void* gamma, const void* beta, float eps,
                              int64_t M, int64_t d, void* y, fsvd_dtype_t dtype, fsvd_stream_t stream) {
     TRY(need_dtype(dtype, false));

@@ -356,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
                 const int row = wm + i * 32 + r;
                 if (row >= g.M || wn + c2 >= g.N) continue;
                 const int b = row / g.S, s = row - b * g.S;
-                const int64_t p = (int64_t)g.seqlens[b] + s;
+                const int64_t p = (g.seqlens ? (int64_t)g.seqlens[b] : 0) + s;
                 const bool write = g.seg == 0 || (p >= 0 && p < g.L_max);
                 if (!write) set_dev_error(g.err, FSVD_DEVERR_KV_OVERFLOW);
                 float x1[8], x2[8];

@@ -116,7 +116,7 @@ struct GemmArgs {
     int S, Hq, Hkv, D;
     float rope_theta;
     int64_t L_max;
-    const int32_t* seqlens;
+    const int32_t* seqlens;      // GEPI_QKV: position of row (b, s) = seqlens[b] + s (NULL: s)
     bf16_t *q_out, *k_cache, *v_cache, *k_out, *v_out;
     int* err;
 };

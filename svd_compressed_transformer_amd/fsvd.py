@@ -60,6 +60,9 @@ _SIGS = {
     "fsvd_decode_attn_dense_kv_ws": (_sz, [_i64] * 6),
     "fsvd_decode_attn_dense_kv": (C.c_int, [_vp, _vp, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _f32, C.c_int,
                                             _vp, C.c_int, _vp, _sz, _vp]),
+    "fsvd_decode_attn_lowrank_kv_ws": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
+    "fsvd_decode_attn_lowrank_kv": (C.c_int, [_vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64,
+                                              _i64, _i64, _f32, _f32, C.c_int, _vp, C.c_int, _vp, _sz, _vp]),
     "fsvd_layernorm": (C.c_int, [_vp, _vp, _vp, _vp, _f32, _i64, _i64, _vp, C.c_int, _vp]),
     "fsvd_seqlens_advance": (C.c_int, [_vp, _i64, _i32, _vp]),
     "fsvd_decoder_layer_ws": (_sz, [C.POINTER(DecoderLayerDesc)]),
@@ -196,6 +199,17 @@ def fsvd_decode_attn_dense_kv(q, k_cache, v_cache, L_max, cache_seqlens, B, Sq, 
     _check(lib().fsvd_decode_attn_dense_kv(_p(q), _p(k_cache), _p(v_cache), L_max, _p(cache_seqlens), B, Sq, Hq, Hkv,
                                            D, softmax_scale, int(causal), _p(out), dtype, _p(ws), ws_bytes,
                                            _s(stream)))
+
+
+def fsvd_decode_attn_lowrank_kv_ws(B, Sq, Hq, Hkv, D, L_max) -> int:
+    return lib().fsvd_decode_attn_lowrank_kv_ws(B, Sq, Hq, Hkv, D, L_max)
+
+
+def fsvd_decode_attn_lowrank_kv(q, zk_cache, zv_cache, ldz, Vt_k, r_k, Vt_v, r_v, L_max, cache_seqlens, B, Sq, Hq,
+                                Hkv, D, rope_theta, softmax_scale, causal, out, dtype, ws, ws_bytes, stream=None):
+    _check(lib().fsvd_decode_attn_lowrank_kv(_p(q), _p(zk_cache), _p(zv_cache), ldz, _p(Vt_k), r_k, _p(Vt_v), r_v,
+                                             L_max, _p(cache_seqlens), B, Sq, Hq, Hkv, D, rope_theta, softmax_scale,
+                                             int(causal), _p(out), dtype, _p(ws), ws_bytes, _s(stream)))
 
 
 def fsvd_layernorm(x, residual, gamma, beta, eps, M, d, y, dtype, stream=None):

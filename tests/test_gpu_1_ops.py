@@ -335,6 +335,49 @@ def test_attention_overflow_flag():
     assert rel(o, O.attention(q, kc, vc, [31], causal=True)) <= BF16_TOL
 
 
+# ----------------------------------------------------------------------------- low-rank-history comparator
+
+
+@pytest.mark.parametrize("B,Sq,Hq,Hkv,D,r_k,r_v,L_max,seqlens,theta", [
+    (2, 1, 4, 2, 128, 40, 24, 150, [100, 37], 1e4),      # decode, GQA, ragged ranks and lengths
+    (1, 1, 8, 8, 64, 16, 64, 70, [69], 1e4),             # the last cache slot
+    (3, 3, 4, 4, 64, 32, 32, 90, [0, 20, 60], 0.0),      # several new tokens (causal), no RoPE
+])
+def test_attention_lowrank_history(B, Sq, Hq, Hkv, D, r_k, r_v, L_max, seqlens, theta):
+    """K/V rebuilt from cached rank-r rows (RoPE at each position), then attention: against the
+    oracle's rebuild and attention.  z rows past each sequence's length are NaN and must not
+    reach the output."""
+    say("attn low-rank history", B, Sq, Hq, Hkv, D, r_k, r_v, L_max, seqlens)
+    rng = np.random.default_rng(17)
+    ldz = max(r_k, r_v) + 8
+    zk = I.round_bf16(rng.standard_normal((B, L_max, ldz)))
+    zv = I.round_bf16(rng.standard_normal((B, L_max, ldz)))
+    for b in range(B):
+        zk[b, seqlens[b] + Sq:] = np.nan
+        zv[b, seqlens[b] + Sq:] = np.nan
+    Vt_k = I.round_bf16(rng.standard_normal((Hkv * D, r_k)) / np.sqrt(r_k))
+    Vt_v = I.round_bf16(rng.standard_normal((Hkv * D, r_v)) / np.sqrt(r_v))
+    q = I.round_bf16(rng.standard_normal((B, Sq, Hq, D)) * 0.3)
+    dq, dzk, dzv, dVk, dVv = to_dev(q), to_dev(zk), to_dev(zv), to_dev(Vt_k), to_dev(Vt_v)
+    sl = torch.tensor(seqlens, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(dq)
+    ws = fsvd.workspace(fsvd.fsvd_decode_attn_lowrank_kv_ws(B, Sq, Hq, Hkv, D, L_max))
+    fsvd.fsvd_decode_attn_lowrank_kv(dq, dzk, dzv, ldz, dVk, r_k, dVv, r_v, L_max, sl, B, Sq, Hq, Hkv, D, theta, 0.0,
+                                     1, out, fsvd.FSVD_BF16, ws, ws.numel())
+    torch.cuda.synchronize()
+    o = from_dev(out)
+    assert np.all(np.isfinite(o))
+    n_max = max(seqlens) + Sq
+    zk0 = np.nan_to_num(zk[:, :n_max, :r_k])
+    zv0 = np.nan_to_num(zv[:, :n_max, :r_v])
+    K, V = O.lowrank_history_kv(zk0, zv0, Vt_k, Vt_v, Hkv, D, theta)
+    ref = O.attention(q, K, V, seqlens, causal=True)
+    err = rel(o, ref)
+    say(f"  err {err:.2e}")
+    assert err <= BF16_TOL
+    assert fsvd.fsvd_poll_device_error(ws) == 0
+
+
 # ----------------------------------------------------------------------------- LayerNorm glue (a7)
 
 

@@ -257,6 +257,27 @@ def pin_qkv_append_and_packing(O):
         assert rel(a_, b_) <= 1e-13
 
 
+def pin_lowrank_history_rebuild(O):
+    """K/V rebuilt from the cached rank-r rows z_k, z_v equal what the current-token path appended
+    to the dense cache for the same tokens (the two layouts hold the same history)."""
+    cfg = _small_decoder()
+    B, S = 2, 6
+    p = I.make_decoder_layer(cfg, B=B, S=S, seed=9, dtype="bf16", random_norm_weights=True)
+    z0 = np.zeros((B, S, cfg.Hkv, cfg.D))
+    _, _, _, kc, vc = O.qkv(p["x"], p["attn_norm_w"], cfg.norm_eps, p["Ut_q"], p["Vt_q"], p["Ut_k"], p["Vt_k"],
+                            p["Ut_v"], p["Vt_v"], cfg.Hq, cfg.Hkv, cfg.D, cfg.rope_theta, z0, z0, np.zeros(B))
+    a = O.rmsnorm(p["x"], p["attn_norm_w"], cfg.norm_eps)
+    zk = a @ np.asarray(p["Ut_k"], dtype=float).T
+    zv = a @ np.asarray(p["Ut_v"], dtype=float).T
+    K, V = O.lowrank_history_kv(zk, zv, p["Vt_k"], p["Vt_v"], cfg.Hkv, cfg.D, cfg.rope_theta)
+    assert rel(K, kc) <= 1e-12 and rel(V, vc) <= 1e-12
+    # without RoPE, K is the plain product
+    K0, _ = O.lowrank_history_kv(zk, zv, p["Vt_k"], p["Vt_v"], cfg.Hkv, cfg.D, 0.0)
+    assert rel(K0, (zk @ np.asarray(p["Vt_k"], dtype=float).T).reshape(B, S, cfg.Hkv, cfg.D)) <= 1e-14
+    # position p of the history is rotated at p: the first position is unrotated
+    assert rel(K[:, 0], K0[:, 0]) <= 1e-14
+
+
 def pin_mlp_packed(O):
     cfg = _small_decoder()
     p = I.make_decoder_layer(cfg, B=2, S=2, seed=6, dtype="bf16", random_norm_weights=True)
@@ -392,7 +413,7 @@ def pin_swift_reuse(O):
 PINS = [pin_lowrank_bruteforce, pin_lowrank_golden, pin_lowrank_fullrank_svd, pin_lowrank_eckart_young,
         pin_zero_padding, pin_rmsnorm, pin_layernorm, pin_rope, pin_activations, pin_attention_matrix,
         pin_attention_special, pin_attention_split_merge, pin_attention_gqa, pin_qkv_append_and_packing,
-        pin_mlp_packed, pin_prefill_then_decode, pin_encoder_layer, pin_swift_golden, pin_swift_closed_form,
+        pin_lowrank_history_rebuild, pin_mlp_packed, pin_prefill_then_decode, pin_encoder_layer, pin_swift_golden, pin_swift_closed_form,
         pin_swift_reuse]
 
 
@@ -467,6 +488,16 @@ def _mut_attention_gqa_modulo(q, k_cache, v_cache, cache_seqlens, causal, scale=
     return o
 
 
+def _mut_history_rope_offset(zk, zv, Vt_k, Vt_v, Hkv, D, rope_theta):
+    zk, zv = np.asarray(zk, dtype=float), np.asarray(zv, dtype=float)
+    B, L, _ = zk.shape
+    k = (zk @ np.asarray(Vt_k, dtype=float).T).reshape(B, L, Hkv, D)
+    v = (zv @ np.asarray(Vt_v, dtype=float).T).reshape(B, L, Hkv, D)
+    if rope_theta:
+        k = O.rope(k, np.arange(1, L + 1)[None, :, None], rope_theta)   # positions counted from 1
+    return k, v
+
+
 def _mut_silu_sign(g):
     g = np.asarray(g, dtype=float)
     return g / (1.0 + np.exp(g))
@@ -489,6 +520,7 @@ MUTANTS = [
     ("attention", _mut_attention_offbyone, pin_attention_special),
     ("attention", _mut_attention_offbyone, pin_prefill_then_decode),
     ("attention", _mut_attention_gqa_modulo, pin_attention_gqa),
+    ("lowrank_history_kv", _mut_history_rope_offset, pin_lowrank_history_rebuild),
     ("silu", _mut_silu_sign, pin_activations),
     ("silu", _mut_silu_sign, pin_mlp_packed),
     ("swift_svd", _mut_swift_ascending, pin_swift_closed_form),
