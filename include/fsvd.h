@@ -22,6 +22,9 @@
  *           packed offline into one tensor, one wide projection, then a split.
  *   [V15-M4] same page, Methodology 4, Per-Layer CUDA Graph Replay: the stable small-batch decode
  *           body of each layer captured once and replayed.
+ *   [SWIFT-2A] "Swift-SVD: Theoretical Optimality Meets Practical Efficiency in Low-Rank LLM
+ *           Compression" (explainer), section 2A: the output covariance aggregated batch by
+ *           batch, one eigendecomposition, the rank-k optimum W V_k V_k^T in closed form.
  *
  * General conventions (apply to every call unless its comment says otherwise)
  *   - Pointers are DEVICE pointers unless marked (host).  Matrices are row-major; "ld" is the row
@@ -220,6 +223,30 @@ fsvd_status_t fsvd_decode_attn_lowrank_kv(const void* q, const void* zk_cache, c
                                           int64_t Hq, int64_t Hkv, int64_t D, float rope_theta,
                                           float softmax_scale, int causal, void* out, fsvd_dtype_t dtype,
                                           void* ws, size_t ws_bytes, fsvd_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Swift-SVD factor production  [SWIFT-2A]
+ * Activation-aware rank-k compression of a linear layer y = x . W (W [d_in, d_out]) from a
+ * stream of calibration inputs X_t [T, d_in], in the page's order:
+ *   1. fsvd_swift_covariance, once per batch: C += Y_t^T . Y_t with Y_t = X_t . W.  C is
+ *      [d_out, d_out] fp32, accumulated across calls (the caller zero-fills it first); it is
+ *      symmetric and only its upper triangle (column >= row, in whole tiles) is written.  Y_t
+ *      is rounded to bf16 before the product; the products accumulate in fp32.
+ *   2. the caller's eigendecomposition of C, eigenvalues descending: the top-k eigenvectors
+ *      V_k [d_out, k] are the right singular vectors of Y = X . W.
+ *   3. fsvd_swift_factors: W_k* = W . V_k . V_k^T as a factor pair in this library's storage,
+ *      Ut = (W . V_k)^T [k, d_in] and Vt = V_k [d_out, k], from VkT = V_k^T [k, d_out] (bf16).
+ * Wt = W^T [d_out, d_in] is the layer's weight in linear-layer storage (K-contiguous, like
+ * Ut and Vt).  X [T, ldx].  T, d_in, d_out and k must be multiples of 8; ldc a multiple of 4.
+ * The workspace holds Y_t^T [d_out, T] (covariance) or W [d_in, d_out] (factors).  bf16 inputs.
+ * ------------------------------------------------------------------------------------------ */
+size_t fsvd_swift_covariance_ws(int64_t T, int64_t d_in, int64_t d_out);
+fsvd_status_t fsvd_swift_covariance(const void* X, int64_t T, int64_t d_in, int64_t ldx, const void* Wt,
+                                    int64_t d_out, float* C, int64_t ldc, void* ws, size_t ws_bytes,
+                                    fsvd_stream_t stream);
+size_t fsvd_swift_factors_ws(int64_t d_in, int64_t d_out);
+fsvd_status_t fsvd_swift_factors(const void* Wt, int64_t d_out, int64_t d_in, const void* VkT, int64_t k,
+                                 void* Ut, void* Vt, void* ws, size_t ws_bytes, fsvd_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * a7. Layer glue: y = LayerNorm(x + residual) * gamma + beta over rows of width d (BERT

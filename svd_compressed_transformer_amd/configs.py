@@ -17,6 +17,9 @@ One JSON line per measurement on stdout:
 - decode_llama3_8b_gqa_b32: the same for 4 Llama-3-8B-shaped GQA layers (32 Q / 8 KV heads,
   d_ff 14336, ranks q 1536, k 512, v 256, o 1024, gate 1024, up 1536, down 512), batch 32,
   history 8192.
+- swift_covariance_4096: one Swift-SVD calibration batch at the Llama-7B projection width
+  (d_in = d_out = 4096, 4096 tokens): Y^T = W^T X^T and C += Y^T Y (upper triangle) on the matrix
+  cores; TFLOP/s of the algorithmic flops (the product and the symmetric half of the covariance).
 - attn_lowrank_history_llama7b_b{1,4}: the decode attention of a Llama-7B-shaped layer over a
   2048-token history, from the dense KV cache against the layout the dense cache replaces
   (rank-1638 rows z_k, z_v cached per token, K and V rebuilt from them every step, then the same
@@ -293,6 +296,30 @@ def run_attn_history(B, history, dev, stream, copies=4):
     return res
 
 
+# ----------------------------------------------------------------------------- Swift-SVD covariance
+
+
+def run_swift_covariance(dev, stream, d=4096, T=4096):
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6)
+    Wt = (torch.randn((d, d), generator=gen, device=dev) / math.sqrt(d)).to(torch.bfloat16)
+    Xs = [torch.randn((T, d), generator=gen, device=dev).to(torch.bfloat16) for _ in range(4)]
+    C = torch.zeros((d, d), dtype=torch.float32, device=dev)
+    ws = fsvd.workspace(fsvd.fsvd_swift_covariance_ws(T, d, d), device=dev)
+    it = {"i": 0}
+
+    def call():
+        X = Xs[it["i"] % len(Xs)]
+        it["i"] += 1
+        fsvd.fsvd_swift_covariance(X, T, d, d, Wt, d, C, d, ws, ws.numel(), stream)
+
+    ms = timed_median(call, stream)
+    flops = 2 * T * d * d + d * (d + 1) * T  # Y^T = W^T X^T, then the upper half of Y^T Y
+    return {"config": "swift_covariance_4096", "d_in": d, "d_out": d, "tokens": T, "ms_per_batch": round(ms, 4),
+            "flops": int(flops), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--only", default="", help="comma-separated subset of the measurement names")
@@ -309,6 +336,7 @@ def main():
     runs.append(("decode_llama3_8b_gqa_b32",
                  lambda: run_decode_stack("decode_llama3_8b_gqa_b32", I.CFG4, dict(I.CFG4.ranks), I.CFG4_BATCH,
                                           I.CFG4_KV_LEN, 4, dev, stream)))
+    runs.append(("swift_covariance_4096", lambda: run_swift_covariance(dev, stream)))
     for B in (1, 4):
         runs.append((f"attn_lowrank_history_llama7b_b{B}", lambda B=B: run_attn_history(B, 2048, dev, stream)))
     only = set(filter(None, args.only.split(",")))

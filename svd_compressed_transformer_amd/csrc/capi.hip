@@ -662,6 +662,62 @@ fsvd_status_t fsvd_decode_attn_lowrank_kv(const void* q, const void* zk_cache, c
                         causal, out, part, ns, (int*)ws, st);
 }
 
+size_t fsvd_swift_covariance_ws(int64_t T, int64_t d_in, int64_t d_out) {
+    (void)d_in;
+    if (T <= 0 || d_out <= 0) return kWsHeader;
+    return kWsHeader + align256((size_t)d_out * T * 2);
+}
+
+fsvd_status_t fsvd_swift_covariance(const void* X, int64_t T, int64_t d_in, int64_t ldx, const void* Wt,
+                                    int64_t d_out, float* C, int64_t ldc, void* ws, size_t ws_bytes,
+                                    fsvd_stream_t stream) {
+    TRY(need_dim(T, "T")); TRY(need_dim(d_in, "d_in")); TRY(need_dim(d_out, "d_out"));
+    TRY(need_vec(T, FSVD_BF16, "T")); TRY(need_vec(d_in, FSVD_BF16, "d_in")); TRY(need_vec(d_out, FSVD_BF16, "d_out"));
+    TRY(need_ld(ldx, d_in, FSVD_BF16, "ldx")); TRY(need_ld(ldc, d_out, FSVD_F32, "ldc"));
+    TRY(need_ptr(X, "X")); TRY(need_ptr(Wt, "Wt")); TRY(need_ptr(C, "C")); TRY(need_ptr(ws, "ws"));
+    const size_t need = fsvd_swift_covariance_ws(T, d_in, d_out);
+    if (ws_bytes < need) return fail(FSVD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+    Carve c(ws);
+    bf16_t* Yt = (bf16_t*)c.take((size_t)d_out * T * 2);
+    hipStream_t st = (hipStream_t)stream;
+    // Y^T = W^T . X^T: rows of Wt against rows of X (both K-contiguous over d_in)
+    GemmArgs g{};
+    g.A = (const bf16_t*)Wt; g.lda = d_in; g.Bm = (const bf16_t*)X; g.ldb = ldx;
+    g.M = (int)d_out; g.N = (int)T; g.K = (int)d_in; g.C = Yt; g.ldc = T; g.err = (int*)ws;
+    TRY(launch_gemm(g, GEPI_STORE, st));
+    // C += Y^T . Y: rows of Y^T against themselves (K-contiguous over T), upper triangle
+    GemmArgs h{};
+    h.A = Yt; h.lda = T; h.Bm = Yt; h.ldb = T;
+    h.M = (int)d_out; h.N = (int)d_out; h.K = (int)T; h.C32 = C; h.ldc = ldc; h.err = (int*)ws;
+    return launch_gemm(h, GEPI_ACC32, st);
+}
+
+size_t fsvd_swift_factors_ws(int64_t d_in, int64_t d_out) {
+    if (d_in <= 0 || d_out <= 0) return kWsHeader;
+    return kWsHeader + align256((size_t)d_in * d_out * 2);
+}
+
+fsvd_status_t fsvd_swift_factors(const void* Wt, int64_t d_out, int64_t d_in, const void* VkT, int64_t k,
+                                 void* Ut, void* Vt, void* ws, size_t ws_bytes, fsvd_stream_t stream) {
+    TRY(need_dim(d_in, "d_in")); TRY(need_dim(d_out, "d_out")); TRY(need_dim(k, "k"));
+    TRY(need_vec(d_in, FSVD_BF16, "d_in")); TRY(need_vec(d_out, FSVD_BF16, "d_out")); TRY(need_vec(k, FSVD_BF16, "k"));
+    if (k > d_out || k > d_in) return fail(FSVD_ERR_INVALID_ARG, "k = %lld exceeds min(d_in, d_out)", (long long)k);
+    TRY(need_ptr(Wt, "Wt")); TRY(need_ptr(VkT, "VkT")); TRY(need_ptr(Ut, "Ut")); TRY(need_ptr(Vt, "Vt"));
+    TRY(need_ptr(ws, "ws"));
+    const size_t need = fsvd_swift_factors_ws(d_in, d_out);
+    if (ws_bytes < need) return fail(FSVD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+    Carve c(ws);
+    bf16_t* W = (bf16_t*)c.take((size_t)d_in * d_out * 2);
+    hipStream_t st = (hipStream_t)stream;
+    TRY(launch_transpose((const bf16_t*)Wt, d_out, d_in, d_in, W, d_out, st));
+    // Ut = V_k^T . W^T: rows of VkT against rows of W (both K-contiguous over d_out)
+    GemmArgs g{};
+    g.A = (const bf16_t*)VkT; g.lda = d_out; g.Bm = W; g.ldb = d_out;
+    g.M = (int)k; g.N = (int)d_in; g.K = (int)d_out; g.C = (bf16_t*)Ut; g.ldc = d_in; g.err = (int*)ws;
+    TRY(launch_gemm(g, GEPI_STORE, st));
+    return launch_transpose((const bf16_t*)VkT, k, d_out, d_out, (bf16_t*)Vt, k, st);
+}
+
 fsvd_status_t fsvd_layernorm(const void* x, const void* residual, const void* gamma, const void* beta, float eps,
                              int64_t M, int64_t d, void* y, fsvd_dtype_t dtype, fsvd_stream_t stream) {
     TRY(need_dtype(dtype, false));

@@ -15,7 +15,8 @@
 //     XCD's L2 work on neighbouring M tiles of one N tile and reuse its B operand.
 // Epilogues: per-row scale (RMSNorm folded after the product), bias + residual, Q/K/V with
 // rotate-half RoPE (the partner column of a pair sits in the same lane) and the dense KV-cache
-// append, SwiGLU (two accumulators, gate and up, with their own A column ranges), GELU.
+// append, SwiGLU (two accumulators, gate and up, with their own A column ranges), GELU, and an
+// fp32 accumulation into C for symmetric products (tiles below the diagonal skipped).
 //
 // Sources: fused low-rank projections ("FlashSVD: Memory-Efficient Inference with Streaming for
 // Low-Rank Models", abstract); prefill kernels shared by every checkpoint family, the packed
@@ -274,6 +275,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
     int tm, tn;
     tile_coords<(BM >= 256 ? 4 : 8)>(tiles_m, tiles_n, &tm, &tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    if constexpr (EPI == GEPI_ACC32) {
+        if (m0 >= n0 + BN) return;  // wholly below the diagonal of a symmetric product (whole workgroup)
+    }
 
     T t;
     t.zero();
@@ -471,11 +475,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
 #pragma unroll
                 for (int q = 0; q < 8; ++q) y[q] = gelu_f(y[q]);
             }
-            bf16_t* cp = g.C + (int64_t)row * g.ldc + col;
-            if (full) {
-                *reinterpret_cast<u32x4*>(cp) = pack8(y);
+            if constexpr (EPI == GEPI_ACC32) {
+                float* cp = g.C32 + (int64_t)row * g.ldc + col;
+                if (full) {
+                    u32x4 lo = *reinterpret_cast<const u32x4*>(cp), hi = *reinterpret_cast<const u32x4*>(cp + 4);
+                    lo.x = __float_as_uint(__uint_as_float(lo.x) + y[0]); lo.y = __float_as_uint(__uint_as_float(lo.y) + y[1]);
+                    lo.z = __float_as_uint(__uint_as_float(lo.z) + y[2]); lo.w = __float_as_uint(__uint_as_float(lo.w) + y[3]);
+                    hi.x = __float_as_uint(__uint_as_float(hi.x) + y[4]); hi.y = __float_as_uint(__uint_as_float(hi.y) + y[5]);
+                    hi.z = __float_as_uint(__uint_as_float(hi.z) + y[6]); hi.w = __float_as_uint(__uint_as_float(hi.w) + y[7]);
+                    *reinterpret_cast<u32x4*>(cp) = lo;
+                    *reinterpret_cast<u32x4*>(cp + 4) = hi;
+                } else {
+                    for (int q = 0; q < 8 && col + q < g.N; ++q) cp[q] += y[q];
+                }
             } else {
-                for (int q = 0; q < 8 && col + q < g.N; ++q) cp[q] = f2bf(y[q]);
+                bf16_t* cp = g.C + (int64_t)row * g.ldc + col;
+                if (full) {
+                    *reinterpret_cast<u32x4*>(cp) = pack8(y);
+                } else {
+                    for (int q = 0; q < 8 && col + q < g.N; ++q) cp[q] = f2bf(y[q]);
+                }
             }
         }
     }
@@ -502,14 +521,20 @@ fsvd_status_t launch_t(const GemmArgs& g, hipStream_t st) {
 template <int EPI>
 fsvd_status_t launch_epi(const GemmArgs& g, hipStream_t st) {
     auto tiles = [&](int bm, int bn) { return ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn); };
-    if constexpr (EPI == GEPI_SWIGLU) {
-        if (tiles(256, 128) >= 256) return launch_t<256, 128, EPI>(g, st);
+    if constexpr (EPI == GEPI_ACC32) {
+        // square tiles; about half of them (below the diagonal) exit at once
+        if (tiles(256, 256) >= 1024) return launch_t<256, 256, EPI>(g, st);
+        return launch_t<128, 128, EPI>(g, st);
     } else {
-        if (tiles(256, 256) >= 512) return launch_t<256, 256, EPI>(g, st);
-        if (tiles(128, 256) >= 256 || (EPI == GEPI_QKV && g.D > 64)) return launch_t<128, 256, EPI>(g, st);
+        if constexpr (EPI == GEPI_SWIGLU) {
+            if (tiles(256, 128) >= 256) return launch_t<256, 128, EPI>(g, st);
+        } else {
+            if (tiles(256, 256) >= 512) return launch_t<256, 256, EPI>(g, st);
+            if (tiles(128, 256) >= 256 || (EPI == GEPI_QKV && g.D > 64)) return launch_t<128, 256, EPI>(g, st);
+        }
+        if (tiles(128, 128) >= 256) return launch_t<128, 128, EPI>(g, st);
+        return launch_t<64, 128, EPI>(g, st);
     }
-    if (tiles(128, 128) >= 256) return launch_t<128, 128, EPI>(g, st);
-    return launch_t<64, 128, EPI>(g, st);
 }
 
 }  // namespace
@@ -524,6 +549,9 @@ fsvd_status_t launch_gemm(const GemmArgs& g, int epi, hipStream_t st) {
         case GEPI_QKV: return launch_epi<GEPI_QKV>(g, st);
         case GEPI_SWIGLU: return launch_epi<GEPI_SWIGLU>(g, st);
         case GEPI_GELU: return launch_epi<GEPI_GELU>(g, st);
+        case GEPI_ACC32:
+            if (g.M != g.N) return fail(FSVD_ERR_INVALID_ARG, "gemm: the symmetric accumulation needs M == N");
+            return launch_epi<GEPI_ACC32>(g, st);
     }
     return fail(FSVD_ERR_UNSUPPORTED, "unknown gemm epilogue %d", epi);
 }

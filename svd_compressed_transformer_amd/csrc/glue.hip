@@ -1,5 +1,6 @@
 // Small kernels around the projections: the offline factor prepack, BERT-style post-norm
-// LayerNorm, the cache-length advance, and the RMSNorm preparation of the MFMA (prefill) path.
+// LayerNorm, the cache-length advance, the RMSNorm preparation of the MFMA (prefill) path and a
+// tiled transpose (weight layouts of the Swift-SVD factor production).
 #include "kernels.h"
 
 namespace fsvd {
@@ -82,6 +83,24 @@ __global__ __launch_bounds__(256) void rms_prep_kernel(const bf16_t* x, const bf
     if (threadIdx.x == 0) rstd[row] = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
 }
 
+// out[c, r] = in[r, c]: a 64 x 64 tile passes through LDS so both the reads (along rows of in)
+// and the writes (along rows of out) are coalesced.  256 threads, 4 rows per pass.
+__global__ __launch_bounds__(256) void transpose_kernel(const bf16_t* __restrict__ in, int64_t rows, int64_t cols,
+                                                        int64_t ld_in, bf16_t* __restrict__ out, int64_t ld_out) {
+    __shared__ bf16_t t[64][66];
+    const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int i = ty; i < 64; i += 4) {
+        const int64_t r = r0 + i, c = c0 + tx;
+        if (r < rows && c < cols) t[i][tx] = in[r * ld_in + c];
+    }
+    __syncthreads();
+    for (int i = ty; i < 64; i += 4) {
+        const int64_t c = c0 + i, r = r0 + tx;
+        if (c < cols && r < rows) out[c * ld_out + r] = t[tx][i];
+    }
+}
+
 }  // namespace
 
 fsvd_status_t launch_prepack(void* dst, int64_t ld_dst, int64_t cols_pad, int64_t row0, const void* src, int64_t rows,
@@ -109,6 +128,15 @@ fsvd_status_t launch_layernorm(const bf16_t* x, const bf16_t* res, const bf16_t*
 fsvd_status_t launch_seqlens_advance(int32_t* sl, int64_t B, int32_t n, hipStream_t st) {
     seqlens_advance_kernel<<<(unsigned)((B + 63) / 64), 64, 0, st>>>(sl, B, n);
     return check_launch("seqlens_advance");
+}
+
+fsvd_status_t launch_transpose(const bf16_t* in, int64_t rows, int64_t cols, int64_t ld_in, bf16_t* out,
+                               int64_t ld_out, hipStream_t st) {
+    if (rows == 0 || cols == 0) return FSVD_OK;
+    if ((rows + 63) / 64 > 65535) return fail(FSVD_ERR_UNSUPPORTED, "transpose: too many rows (%lld)", (long long)rows);
+    const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+    transpose_kernel<<<grid, 256, 0, st>>>(in, rows, cols, ld_in, out, ld_out);
+    return check_launch("transpose");
 }
 
 fsvd_status_t launch_rms_prep(const bf16_t* x, const bf16_t* w, float eps, int64_t M, int64_t d, bf16_t* xn,

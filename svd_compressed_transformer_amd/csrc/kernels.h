@@ -101,6 +101,8 @@ enum GemmEpi : int {
     GEPI_QKV = 2,      // column segments q | k | v with RoPE and cache append
     GEPI_SWIGLU = 3,   // dual B operand: C = SiLU(A.Bg^T) * (A.Bu^T)
     GEPI_GELU = 4,
+    GEPI_ACC32 = 5,    // C32[m, n] += acc (fp32); square tiles, those wholly below the diagonal are
+                       // skipped (symmetric products A . A^T: the upper triangle is computed)
 };
 struct GemmArgs {
     // C[M, N] = A[M, a_col_off : a_col_off + K] . B[N, K]^T ; bf16 operands, K-contiguous, fp32 accumulate
@@ -117,10 +119,14 @@ struct GemmArgs {
     float rope_theta;
     int64_t L_max;
     const int32_t* seqlens;      // GEPI_QKV: position of row (b, s) = seqlens[b] + s (NULL: s)
+    float* C32;                  // GEPI_ACC32: fp32 accumulator [M, ldc]
     bf16_t *q_out, *k_cache, *v_cache, *k_out, *v_out;
     int* err;
 };
 fsvd_status_t launch_gemm(const GemmArgs& g, int epi, hipStream_t st);
+// out[c, r] = in[r, c] for r < rows, c < cols (bf16, through 64 x 64 LDS tiles)
+fsvd_status_t launch_transpose(const bf16_t* in, int64_t rows, int64_t cols, int64_t ld_in, bf16_t* out,
+                               int64_t ld_out, hipStream_t st);
 // per-row inverse RMS of x [M, d] (with norm weight folded by the caller) -> rstd [M], and
 // xn = bf16(x * w) [M, d]
 fsvd_status_t launch_rms_prep(const bf16_t* x, const bf16_t* w, float eps, int64_t M, int64_t d, bf16_t* xn,

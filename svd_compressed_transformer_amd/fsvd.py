@@ -63,6 +63,10 @@ _SIGS = {
     "fsvd_decode_attn_lowrank_kv_ws": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
     "fsvd_decode_attn_lowrank_kv": (C.c_int, [_vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64,
                                               _i64, _i64, _f32, _f32, C.c_int, _vp, C.c_int, _vp, _sz, _vp]),
+    "fsvd_swift_covariance_ws": (_sz, [_i64, _i64, _i64]),
+    "fsvd_swift_covariance": (C.c_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
+    "fsvd_swift_factors_ws": (_sz, [_i64, _i64]),
+    "fsvd_swift_factors": (C.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "fsvd_layernorm": (C.c_int, [_vp, _vp, _vp, _vp, _f32, _i64, _i64, _vp, C.c_int, _vp]),
     "fsvd_seqlens_advance": (C.c_int, [_vp, _i64, _i32, _vp]),
     "fsvd_decoder_layer_ws": (_sz, [C.POINTER(DecoderLayerDesc)]),
@@ -210,6 +214,22 @@ def fsvd_decode_attn_lowrank_kv(q, zk_cache, zv_cache, ldz, Vt_k, r_k, Vt_v, r_v
     _check(lib().fsvd_decode_attn_lowrank_kv(_p(q), _p(zk_cache), _p(zv_cache), ldz, _p(Vt_k), r_k, _p(Vt_v), r_v,
                                              L_max, _p(cache_seqlens), B, Sq, Hq, Hkv, D, rope_theta, softmax_scale,
                                              int(causal), _p(out), dtype, _p(ws), ws_bytes, _s(stream)))
+
+
+def fsvd_swift_covariance_ws(T, d_in, d_out) -> int:
+    return lib().fsvd_swift_covariance_ws(T, d_in, d_out)
+
+
+def fsvd_swift_covariance(X, T, d_in, ldx, Wt, d_out, C, ldc, ws, ws_bytes, stream=None):
+    _check(lib().fsvd_swift_covariance(_p(X), T, d_in, ldx, _p(Wt), d_out, _p(C), ldc, _p(ws), ws_bytes, _s(stream)))
+
+
+def fsvd_swift_factors_ws(d_in, d_out) -> int:
+    return lib().fsvd_swift_factors_ws(d_in, d_out)
+
+
+def fsvd_swift_factors(Wt, d_out, d_in, VkT, k, Ut, Vt, ws, ws_bytes, stream=None):
+    _check(lib().fsvd_swift_factors(_p(Wt), d_out, d_in, _p(VkT), k, _p(Ut), _p(Vt), _p(ws), ws_bytes, _s(stream)))
 
 
 def fsvd_layernorm(x, residual, gamma, beta, eps, M, d, y, dtype, stream=None):
