@@ -123,6 +123,88 @@ __host__ __device__ __forceinline__ bool seg_paired(int epi, int kind) {
 // wave sets (each wave reads one activation vector, z_gate or z_up), joined in the LDS combine
 __host__ __device__ __forceinline__ int wave_sets(int epi) { return epi == EPI_SWIGLU ? 2 : 1; }
 
+// Epilogue shared by the row-dot kernels: output unit j of unit group g for activation row m, from
+// the fully reduced values val(g, h, r, m) (h: wave set, r: factor row within the group) and, in
+// phase 1 with the RMSNorm prologue, the activation row's sum of squares ssq(g, m).  A RoPE pair's
+// second row sits pair_off rows after its first.  Threads tid, tid + nthreads, ... share the
+// (g, j, m) triples of the workgroup.
+template <typename T, int EPI, class Val, class Ssq>
+__device__ __forceinline__ void rowdot_epilogue(const RowdotArgs& a, const RowdotSeg& sg, int unit_base, int ngroups,
+                                                int upw, int pair_off, int n_units, int tid, int nthreads, Val val,
+                                                Ssq ssq) {
+    const int M = a.M;
+    const int halfD = a.D >> 1;
+    const int total = ngroups * upw * M;
+    for (int idx = tid; idx < total; idx += nthreads) {
+        const int g = idx / (upw * M);
+        const int rem = idx - g * upw * M;
+        const int j = rem / M;           // unit within the wave
+        const int m = rem - j * M;       // activation row
+        const int u = unit_base + g * upw + j;
+        if (u >= n_units) continue;
+        if constexpr (EPI == EPI_Z) {
+            float v = val(g, 0, j, m);
+            if (a.norm) {
+                const float sq = ssq(g, m);
+                v *= 1.0f / sqrtf(sq / (float)a.norm_K + a.norm_eps);
+            }
+            store_t<T>(sg.out, (int64_t)m * sg.ldo + u, v);
+        } else if constexpr (EPI == EPI_LINEAR) {
+            float v = val(g, 0, j, m);
+            if (a.bias) v += load_t<T>(a.bias, u);
+            if (a.residual) v += load_t<T>(a.residual, (int64_t)m * a.ldr + u);
+            store_t<T>(sg.out, (int64_t)m * sg.ldo + u, v);
+        } else if constexpr (EPI == EPI_GELU) {
+            store_t<T>(sg.out, (int64_t)m * sg.ldo + u, gelu_f(val(g, 0, j, m)));
+        } else if constexpr (EPI == EPI_SWIGLU) {
+            const float gv = val(g, 0, j, m), uv = val(g, 1, j, m);
+            store_t<T>(sg.out, (int64_t)m * sg.ldo + u, silu_f(gv) * uv);
+        } else if constexpr (EPI == EPI_QKV) {
+            const int b = m / a.S, s = m - b * a.S;
+            const int64_t p = (int64_t)a.seqlens[b] + s;
+            const bool in_cache = p >= 0 && p < a.L_max;
+            if (sg.kind == SEG_V) {
+                const bf16_t bits = f2bf(val(g, 0, j, m));
+                const int hd = a.Hkv * a.D;
+                if (in_cache) a.v_cache[((int64_t)b * a.L_max + p) * hd + u] = bits;
+                else set_dev_error(a.err, FSVD_DEVERR_KV_OVERFLOW);
+                if (a.v_out) a.v_out[(int64_t)m * hd + u] = bits;
+            } else {
+                const float x1 = val(g, 0, j, m), x2 = val(g, 0, j + pair_off, m);
+                const int h = u / halfD, i = u - h * halfD;
+                const int n1 = h * a.D + i, n2 = n1 + halfD;
+                float y1 = x1, y2 = x2;
+                if (a.rope_theta > 0.f) {
+                    float c, sn;
+                    rope_cs(p, i, a.D, a.rope_theta, &c, &sn);
+                    y1 = x1 * c - x2 * sn;
+                    y2 = x2 * c + x1 * sn;
+                }
+                const bf16_t b1 = f2bf(y1), b2 = f2bf(y2);
+                if (sg.kind == SEG_Q) {
+                    bf16_t* q = reinterpret_cast<bf16_t*>(sg.out);
+                    q[(int64_t)m * sg.ldo + n1] = b1;
+                    q[(int64_t)m * sg.ldo + n2] = b2;
+                } else {
+                    const int hd = a.Hkv * a.D;
+                    if (in_cache) {
+                        bf16_t* kc = a.k_cache + ((int64_t)b * a.L_max + p) * hd;
+                        kc[n1] = b1;
+                        kc[n2] = b2;
+                    } else {
+                        set_dev_error(a.err, FSVD_DEVERR_KV_OVERFLOW);
+                    }
+                    if (a.k_out) {
+                        a.k_out[(int64_t)m * hd + n1] = b1;
+                        a.k_out[(int64_t)m * hd + n2] = b2;
+                    }
+                }
+            }
+        }
+    }
+}
+
+
 template <typename T, int BMAX, int EPI>
 __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const RowdotArgs a) {
     constexpr int E = Vec<T>::E;
@@ -295,75 +377,170 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
         return s;
     };
 
-    const int ngroups = a.waves / (NS * ksplit);
-    const int total = ngroups * upw * M;
-    for (int idx = tid; idx < total; idx += 64 * a.waves) {
-        const int g = idx / (upw * M);
-        const int rem = idx - g * upw * M;
-        const int j = rem / M;           // unit within the wave
-        const int m = rem - j * M;       // activation row
-        const int u = (bid - sg.blk_begin) * sg.units_per_blk + g * upw + j;
-        if (u >= n_units) continue;
-        if constexpr (EPI == EPI_Z) {
-            float v = val(g, 0, j, m);
-            if (a.norm) {
-                const float sq = val(g, 0, kR, m);
-                v *= 1.0f / sqrtf(sq / (float)a.norm_K + a.norm_eps);
-            }
-            store_t<T>(sg.out, (int64_t)m * sg.ldo + u, v);
-        } else if constexpr (EPI == EPI_LINEAR) {
-            float v = val(g, 0, j, m);
-            if (a.bias) v += load_t<T>(a.bias, u);
-            if (a.residual) v += load_t<T>(a.residual, (int64_t)m * a.ldr + u);
-            store_t<T>(sg.out, (int64_t)m * sg.ldo + u, v);
-        } else if constexpr (EPI == EPI_GELU) {
-            store_t<T>(sg.out, (int64_t)m * sg.ldo + u, gelu_f(val(g, 0, j, m)));
-        } else if constexpr (EPI == EPI_SWIGLU) {
-            const float gv = val(g, 0, j, m), uv = val(g, 1, j, m);
-            store_t<T>(sg.out, (int64_t)m * sg.ldo + u, silu_f(gv) * uv);
-        } else if constexpr (EPI == EPI_QKV) {
-            const int b = m / a.S, s = m - b * a.S;
-            const int64_t p = (int64_t)a.seqlens[b] + s;
-            const bool in_cache = p >= 0 && p < a.L_max;
-            if (sg.kind == SEG_V) {
-                const bf16_t bits = f2bf(val(g, 0, j, m));
-                const int hd = a.Hkv * a.D;
-                if (in_cache) a.v_cache[((int64_t)b * a.L_max + p) * hd + u] = bits;
-                else set_dev_error(a.err, FSVD_DEVERR_KV_OVERFLOW);
-                if (a.v_out) a.v_out[(int64_t)m * hd + u] = bits;
-            } else {
-                const float x1 = val(g, 0, j, m), x2 = val(g, 0, j + kH, m);
-                const int h = u / halfD, i = u - h * halfD;
-                const int n1 = h * a.D + i, n2 = n1 + halfD;
-                float y1 = x1, y2 = x2;
-                if (a.rope_theta > 0.f) {
-                    float c, sn;
-                    rope_cs(p, i, a.D, a.rope_theta, &c, &sn);
-                    y1 = x1 * c - x2 * sn;
-                    y2 = x2 * c + x1 * sn;
-                }
-                const bf16_t b1 = f2bf(y1), b2 = f2bf(y2);
-                if (sg.kind == SEG_Q) {
-                    bf16_t* q = reinterpret_cast<bf16_t*>(sg.out);
-                    q[(int64_t)m * sg.ldo + n1] = b1;
-                    q[(int64_t)m * sg.ldo + n2] = b2;
-                } else {
-                    const int hd = a.Hkv * a.D;
-                    if (in_cache) {
-                        bf16_t* kc = a.k_cache + ((int64_t)b * a.L_max + p) * hd;
-                        kc[n1] = b1;
-                        kc[n2] = b2;
-                    } else {
-                        set_dev_error(a.err, FSVD_DEVERR_KV_OVERFLOW);
-                    }
-                    if (a.k_out) {
-                        a.k_out[(int64_t)m * hd + n1] = b1;
-                        a.k_out[(int64_t)m * hd + n2] = b2;
-                    }
-                }
+    rowdot_epilogue<T, EPI>(a, sg, (bid - sg.blk_begin) * sg.units_per_blk, a.waves / (NS * ksplit), upw, kH, n_units,
+                            tid, 64 * a.waves, val, [&](int g, int m) { return val(g, 0, kR, m); });
+}
+
+// Skinny-MFMA variant for 9..32 activation rows (bf16).  Past about 8 rows the row-dot's dot
+// products, which grow with the number of activation rows while the factor bytes do not, make
+// the kernel vector-ALU bound (measured on MI355X: the instruction count and the time grow with
+// the batch).  Here a wave owns a tile of 16 factor rows and its products run on the matrix
+// cores as v_mfma_f32_16x16x32_bf16: the B operand is 16 factor rows x 32 k (lane l holds 8
+// consecutive k of row l % 16 at k group l / 16, so one load instruction reads 64 contiguous bytes
+// of each row), the A operand 16 activation rows x 32 k with the same k groups (MB = 2 tiles for
+// 17..32 rows); C[m][row] accumulates in fp32.  The factor stream, the k split over waves, the
+// RMSNorm statistics and the epilogues are those of the row-dot; the partial tiles of the waves
+// that split k are summed from LDS.
+typedef __bf16 bf16x8_m __attribute__((ext_vector_type(8)));
+typedef float f32x4_m __attribute__((ext_vector_type(4)));
+constexpr int kMfmaRows = 16;  // factor rows per wave tile
+constexpr int kMfmaSteps = 8;  // 32-wide k steps whose loads one pass keeps in flight (16 activation rows)
+
+template <int MB, int EPI>
+__global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
+    using T = bf16_t;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int bid = blockIdx.x;
+    const int si = EPI != EPI_QKV ? 0
+                   : ((a.nseg > 2 && bid >= a.seg[2].blk_begin) ? 2 : ((a.nseg > 1 && bid >= a.seg[1].blk_begin) ? 1 : 0));
+    const RowdotSeg sg = EPI != EPI_QKV ? a.seg[0] : (si == 0 ? a.seg[0] : (si == 1 ? a.seg[1] : a.seg[2]));
+
+    const bool paired = seg_paired(EPI, sg.kind);
+    const int upw = paired ? kMfmaRows / 2 : kMfmaRows;           // output units per wave tile
+    const int n_units = (EPI == EPI_QKV && paired) ? sg.N / 2 : sg.N;
+    const int ksplit = a.ksplit;
+    constexpr int NS = EPI == EPI_SWIGLU ? 2 : 1;
+    const int grp = wave / (NS * ksplit);
+    const int half = (wave / ksplit) % NS;
+    const int ks = wave % ksplit;
+    const int unit0 = (bid - sg.blk_begin) * sg.units_per_blk + grp * upw;
+    const int halfD = a.D >> 1;
+
+    // this lane's factor row (column rj of the B operand) and k group kq
+    const int rj = lane & 15, kq = lane >> 4;
+    const int mat = EPI == EPI_SWIGLU ? half : 0;
+    int u, n;
+    if (paired) {  // rows 0..7: first halves of 8 RoPE pairs, rows 8..15: their partners
+        u = unit0 + (rj & 7);
+        const int h = u / halfD, i = u - h * halfD;
+        n = h * a.D + i + (rj >> 3) * halfD;
+    } else {
+        u = unit0 + rj;
+        n = u;
+    }
+    const bool valid = u < n_units;
+    const char* W = reinterpret_cast<const char*>(mat ? sg.W2 : sg.W);
+    const int64_t ldw = mat ? sg.ldw2 : sg.ldw;
+    const char* wrow = W + (valid ? (int64_t)n * ldw * (int64_t)sizeof(T) : 0);
+
+    constexpr int SE = 32;  // k per MFMA step
+    const int kmax = (EPI == EPI_SWIGLU) ? max(sg.K, sg.K2) : sg.K;
+    const int st_per = ((kmax + SE - 1) / SE + ksplit - 1) / ksplit;
+    const int k_lo = ks * st_per * SE;
+    const int k_hi = min(kmax, k_lo + st_per * SE);
+    const int kw = EPI == EPI_SWIGLU ? (half ? sg.K2 : sg.K) : sg.K;
+    const int k_end = min(k_hi, kw);
+    const int kc_max = kw - 8;
+
+    const int M = a.M;
+    const int64_t lda_b = a.lda * (int64_t)sizeof(T);
+    const int aoff = mat ? sg.act_off2 : sg.act_off;
+    const bool norm = (EPI == EPI_Z) && a.norm;
+    const bool norm_w = norm && a.norm_w != nullptr;
+    const char* arow[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        arow[mb] = reinterpret_cast<const char*>(a.act) + min(mb * 16 + rj, M - 1) * lda_b + (int64_t)aoff * sizeof(T);
+    const char* nwp = norm_w ? reinterpret_cast<const char*>(a.norm_w) : arow[0];
+
+    f32x4_m acc[MB];
+    float ss[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        acc[mb] = f32x4_m{0.f, 0.f, 0.f, 0.f};
+        ss[mb] = 0.f;
+    }
+    const int nsteps = k_hi > k_lo ? (k_hi - k_lo + SE - 1) / SE : 0;
+    auto pass = [&](auto nu_c, int s0) {
+        constexpr int NU = decltype(nu_c)::value;
+        u32x4 wv[NU], nw[NU], av[NU][MB];
+#pragma unroll
+        for (int q = 0; q < NU; ++q) {
+            const int k = k_lo + (s0 + q) * SE + kq * 8;
+            const int64_t kc = (int64_t)min(k, kc_max) * sizeof(T);
+            wv[q] = ldg16_stream(wrow + kc);
+            if (norm_w) nw[q] = ldg16(nwp + kc);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) av[q][mb] = ldg16(arow[mb] + kc);
+        }
+        if (k_lo + (s0 + NU) * SE > k_end) {  // wave-uniform: the pass reaches past k_end
+#pragma unroll
+            for (int q = 0; q < NU; ++q) {
+                const bool ok = k_lo + (s0 + q) * SE + kq * 8 < k_end;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) av[q][mb] = ok ? av[q][mb] : u32x4{0u, 0u, 0u, 0u};
             }
         }
+#pragma unroll
+        for (int q = 0; q < NU; ++q) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                u32x4 x = av[q][mb];
+                if constexpr (EPI == EPI_Z) {
+                    if (norm) {
+                        ss[mb] = vsq(x, ss[mb], T());
+                        if (norm_w) x = vmulw(x, nw[q]);
+                    }
+                }
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_m, x),
+                                                                   __builtin_bit_cast(bf16x8_m, wv[q]), acc[mb], 0, 0, 0);
+            }
+        }
+    };
+    // Whole passes of U steps (a shorter last pass would cost one round trip per step); steps past
+    // the slice load clamped addresses (cache hits) and are zeroed by the activation mask.
+    constexpr int U = MB == 1 ? kMfmaSteps : kMfmaSteps / 2;
+    for (int s0 = 0; s0 < nsteps; s0 += U) pass(std::integral_constant<int, U>(), s0);
+
+    // C tile of this wave: lane holds C[m = 16 mb + 4 kq + e][row rj]; the k-split waves of a unit
+    // group are summed from LDS.  Sums of squares: over the 4 k groups of an activation row.
+    __shared__ float red[kMaxWaves][32][kMfmaRows];
+    __shared__ float red_ss[kMaxWaves][32];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[wave][mb * 16 + kq * 4 + e][rj] = acc[mb][e];
+    if (norm) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            float v = ss[mb];
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            if (kq == 0) red_ss[wave][mb * 16 + rj] = v;
+        }
     }
+    __syncthreads();
+
+    if constexpr (EPI == EPI_LINEAR) {
+        if (a.adv_seqlens != nullptr && bid == 0 && tid < a.adv_B) a.adv_seqlens[tid] += a.adv_n;
+    }
+    auto sum_waves = [&](int w0, auto get) -> float {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < kMaxWaves; ++w) {
+            const float t = get(min(w0 + w, kMaxWaves - 1));
+            s += w < ksplit ? t : 0.f;
+        }
+        return s;
+    };
+    auto val = [&](int g, int h, int r, int m) -> float {
+        return sum_waves((g * NS + h) * ksplit, [&](int w) { return red[w][m][r]; });
+    };
+    auto ssq = [&](int g, int m) -> float {
+        return sum_waves(g * NS * ksplit, [&](int w) { return red_ss[w][m]; });
+    };
+    rowdot_epilogue<T, EPI>(a, sg, (bid - sg.blk_begin) * sg.units_per_blk, a.waves / (NS * ksplit), upw,
+                            kMfmaRows / 2, n_units, tid, 64 * a.waves, val, ssq);
 }
 
 template <typename T, int EPI>
@@ -380,30 +557,49 @@ fsvd_status_t launch_b(const RowdotArgs& a, int grid, hipStream_t st) {
 
 }  // namespace
 
-int rowdot_plan(RowdotArgs& a, int epi) {
+namespace {
+
+// bf16 launches of 9..32 activation rows go to the matrix cores, except reductions longer than
+// 8192 over at most 16 rows, where the 16-row tiles leave too few waves (measured on MI355X: the
+// down projection's phase 1, K = 11008, is faster on v_dot2 at 16 rows and even at 32).
+#ifndef FSVD_RD_MFMA_MIN_M
+#define FSVD_RD_MFMA_MIN_M 9
+#endif
+bool use_mfma(const RowdotArgs& a, int epi, fsvd_dtype_t dtype) {
+    if (dtype != FSVD_BF16 || a.M < FSVD_RD_MFMA_MIN_M) return false;
+    int kmax = 0;
+    for (int i = 0; i < a.nseg; ++i) kmax = std::max(kmax, std::max(a.seg[i].K, epi == EPI_SWIGLU ? a.seg[i].K2 : 0));
+    return !(a.M <= 16 && kmax > 8192);
+}
+
+// rows: factor rows per wave (kR for the v_dot2 kernel, 16 for the MFMA kernel)
+int plan_rows(RowdotArgs& a, int epi, int rows, bool mfma) {
     // Reduction split: about 1024 elements per wave for long reductions (one or two load passes),
     // then doubled while the launch has fewer than ~2048 waves.  4 waves per workgroup, 8 when the
     // split needs them.
+    const int rh = rows / 2;
     int kmax = 0, units = 0;
     for (int i = 0; i < a.nseg; ++i) {
         const RowdotSeg& s = a.seg[i];
         const bool paired = seg_paired(epi, s.kind);
         kmax = std::max(kmax, std::max(s.K, epi == EPI_SWIGLU ? s.K2 : 0));
         const int u = (epi == EPI_QKV && paired) ? s.N / 2 : s.N;
-        units += wave_sets(epi) * (paired ? (u + kH - 1) / kH : (u + kR - 1) / kR);  // waves without split
+        units += wave_sets(epi) * (paired ? (u + rh - 1) / rh : (u + rows - 1) / rows);  // waves without split
     }
+    // (measured on MI355X for the matrix-core variant too: a deeper split with 16-wave workgroups
+    // and one pass per wave was slower than this)
     int ksplit = 1;
     while (ksplit < 8 && (kmax + ksplit - 1) / ksplit > FSVD_RD_KPW && kmax / (ksplit * 2) >= 256) ksplit *= 2;
     while (ksplit < 8 && (int64_t)units * ksplit < FSVD_RD_WAVES && kmax / (ksplit * 2) >= 256) ksplit *= 2;
-    if (a.M > 16) ksplit = std::min(ksplit, 4);  // the 32-row variant runs 4-wave workgroups
-    if (epi == EPI_SWIGLU) ksplit = std::min(ksplit, a.M > 16 ? 2 : 4);  // two wave sets per group
+    if (!mfma && a.M > 16) ksplit = std::min(ksplit, 4);  // the 32-row variant runs 4-wave workgroups
+    if (epi == EPI_SWIGLU) ksplit = std::min(ksplit, (!mfma && a.M > 16) ? 2 : 4);  // two wave sets per group
     a.ksplit = ksplit;
     a.waves = wave_sets(epi) * ksplit > 4 ? 8 : 4;
     int blk = 0;
     for (int i = 0; i < a.nseg; ++i) {
         RowdotSeg& s = a.seg[i];
         const bool paired = seg_paired(epi, s.kind);
-        const int upw = paired ? kH : kR;
+        const int upw = paired ? rh : rows;
         const int n_units = (epi == EPI_QKV && paired) ? s.N / 2 : s.N;
         s.units_per_blk = (a.waves / (wave_sets(epi) * ksplit)) * upw;
         s.blk_begin = blk;
@@ -412,17 +608,41 @@ int rowdot_plan(RowdotArgs& a, int epi) {
     return blk;
 }
 
+template <int EPI>
+fsvd_status_t launch_mfma(const RowdotArgs& a, int grid, hipStream_t st) {
+    if (a.M <= 16) rowdot_mfma_kernel<1, EPI><<<grid, 64 * a.waves, 0, st>>>(a);
+    else rowdot_mfma_kernel<2, EPI><<<grid, 64 * a.waves, 0, st>>>(a);
+    return check_launch("rowdot_mfma");
+}
+
+}  // namespace
+
+int rowdot_plan(RowdotArgs& a, int epi, fsvd_dtype_t dtype) {
+    const bool mfma = use_mfma(a, epi, dtype);
+    return plan_rows(a, epi, mfma ? kMfmaRows : kR, mfma);
+}
+
 fsvd_status_t launch_rowdot(const RowdotArgs& a, int epi, fsvd_dtype_t dtype, hipStream_t st) {
     RowdotArgs c = a;
-    const int grid = rowdot_plan(c, epi);
-    if (grid <= 0) return FSVD_OK;
     if (c.M < 1 || c.M > 32) return fail(FSVD_ERR_UNSUPPORTED, "row-dot path supports 1..32 activation rows, got %d", c.M);
+    const int grid = rowdot_plan(c, epi, dtype);
+    if (grid <= 0) return FSVD_OK;
     if (dtype == FSVD_F32) {
         switch (epi) {
             case EPI_Z: return launch_b<float, EPI_Z>(c, grid, st);
             case EPI_LINEAR: return launch_b<float, EPI_LINEAR>(c, grid, st);
             default: return fail(FSVD_ERR_UNSUPPORTED, "fp32 row-dot supports the plain linear epilogues only");
         }
+    }
+    if (use_mfma(c, epi, dtype)) {
+        switch (epi) {
+            case EPI_Z: return launch_mfma<EPI_Z>(c, grid, st);
+            case EPI_LINEAR: return launch_mfma<EPI_LINEAR>(c, grid, st);
+            case EPI_QKV: return launch_mfma<EPI_QKV>(c, grid, st);
+            case EPI_SWIGLU: return launch_mfma<EPI_SWIGLU>(c, grid, st);
+            case EPI_GELU: return launch_mfma<EPI_GELU>(c, grid, st);
+        }
+        return fail(FSVD_ERR_UNSUPPORTED, "unknown row-dot epilogue %d", epi);
     }
     switch (epi) {
         case EPI_Z: return launch_b<bf16_t, EPI_Z>(c, grid, st);

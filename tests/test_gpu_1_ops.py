@@ -108,7 +108,11 @@ def test_linear_cfg0_fp32():
 
 
 @pytest.mark.parametrize("M,K,r,N", [(1, 512, 64, 256), (3, 1000, 40, 1032), (7, 4096, 1640, 520),
-                                     (16, 2048, 24, 3000), (32, 768, 392, 768), (5, 8, 8, 8)])
+                                     (16, 2048, 24, 3000), (32, 768, 392, 768), (5, 8, 8, 8),
+                                     # 9..32 rows run on the matrix cores: one and two 16-row tiles,
+                                     # ragged K, rank and N
+                                     (9, 4096, 1640, 4096), (17, 1000, 40, 1032), (24, 11008, 1640, 520),
+                                     (32, 8, 8, 8)])
 def test_linear_bf16_decode_shapes(M, K, r, N):
     say("bf16 linear", M, K, r, N)
     x, Ut, Vt, b, res = _linear_case(M, K, r, N, "bf16", seed=M + K)
@@ -116,19 +120,20 @@ def test_linear_bf16_decode_shapes(M, K, r, N):
     assert rel(y, O.lowrank_linear(x, Ut, Vt)) <= BF16_TOL
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_linear_bias_residual_inplace(dtype):
-    say("linear bias+residual", dtype)
-    x, Ut, Vt, b, res = _linear_case(4, 640, 48, 392, dtype, seed=9, bias=True, residual=True)
+@pytest.mark.parametrize("dtype,M", [("bf16", 4), ("f32", 4), ("bf16", 20)])
+def test_linear_bias_residual_inplace(dtype, M):
+    say("linear bias+residual", dtype, M)
+    x, Ut, Vt, b, res = _linear_case(M, 640, 48, 392, dtype, seed=9, bias=True, residual=True)
     ref = O.lowrank_linear(x, Ut, Vt, bias=b, residual=res)
     tol = BF16_TOL if dtype == "bf16" else F32_TOL
     assert rel(_run_linear(x, Ut, Vt, b, res, dtype), ref) <= tol
     assert rel(_run_linear(x, Ut, Vt, b, res, dtype, inplace=True), ref) <= tol
 
 
-def test_linear_deterministic():
-    x, Ut, Vt, _, _ = _linear_case(8, 4096, 1640, 4096, "bf16", seed=1)
-    say("linear determinism 8x4096x1640x4096")
+@pytest.mark.parametrize("M", [8, 24])
+def test_linear_deterministic(M):
+    x, Ut, Vt, _, _ = _linear_case(M, 4096, 1640, 4096, "bf16", seed=1)
+    say("linear determinism", M, "x4096x1640x4096")
     y1 = _run_linear(x, Ut, Vt, None, None, "bf16")
     y2 = _run_linear(x, Ut, Vt, None, None, "bf16")
     assert np.array_equal(y1, y2)
@@ -248,7 +253,7 @@ def test_mlp_swiglu(cfg, M):
         assert rel(from_dev(y), ref) <= BF16_TOL
 
 
-@pytest.mark.parametrize("M", [1, 8])
+@pytest.mark.parametrize("M", [1, 8, 12, 32])
 def test_mlp_gelu(M):
     cfg = I.EncoderLayerConfig(name="enc-small", d=256, H=4, D=64, d_ff=512,
                                ranks={"q": 64, "k": 64, "v": 64, "o": 64, "up": 104, "down": 80})
