@@ -1,6 +1,7 @@
 // C-ABI front of the fused low-rank layer library: argument validation, workspace carving,
 // dispatch between the decode row-dot kernels (M <= 32 activation rows) and the bf16 MFMA
 // kernels (larger M), the whole decoder layer, and its per-layer hipGraph.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -163,6 +164,7 @@ fsvd_status_t enqueue_qkv(const QkvDims& q, const void* x, bool norm, const void
         b.nseg = 3;
         b.act = wb.z; b.lda = rtot; b.M = M; b.err = wb.err;
         b.S = q.S; b.Hq = q.Hq; b.Hkv = q.Hkv; b.D = q.D; b.rope_theta = q.theta; b.L_max = q.L_max;
+        b.rope_base = q.theta > 0.f ? std::pow((double)q.theta, -2.0 / (double)q.D) : 0.0;
         b.seqlens = seqlens; b.k_cache = (bf16_t*)kc; b.v_cache = (bf16_t*)vc;
         b.k_out = (bf16_t*)k_out; b.v_out = (bf16_t*)v_out;
         RowdotSeg& s0 = b.seg[0];

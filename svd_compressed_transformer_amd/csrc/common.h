@@ -110,14 +110,19 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 __device__ __forceinline__ float gelu_f(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); }
 
-// RoPE angle for pair i of a head of width D at position p: p * theta^(-2i/D), reduced mod 2*pi in
-// double so long positions keep fp32 accuracy in sin/cos.
-__device__ __forceinline__ void rope_cs(int64_t p, int i, int D, float theta, float* c, float* s) {
-    double inv = exp2(-2.0 * (double)i / (double)D * log2((double)theta));
-    double ang = (double)p * inv;
-    const double two_pi = 6.283185307179586476925286766559;
-    ang = ang - two_pi * floor(ang / two_pi);
-    sincosf((float)ang, s, c);
+// RoPE angle for pair i at position p: p * base^i with base = theta^(-2/D) (computed once on the
+// host in double).  base^i by binary exponentiation in double (i < 64: at most 12 products, a few
+// ulp), the angle reduced modulo 2 pi in double so long positions keep fp32 accuracy in sin/cos.
+__device__ __forceinline__ void rope_cs(int64_t p, int i, double base, float* c, float* s) {
+    double inv = 1.0, sq = base;
+#pragma unroll
+    for (int bit = 0; bit < 6; ++bit) {
+        if (i & (1 << bit)) inv *= sq;
+        sq *= sq;
+    }
+    const double rev = (double)p * inv * 0.15915494309189533576888376337251;  // revolutions
+    const float ang = (float)((rev - floor(rev)) * 6.283185307179586476925286766559);
+    sincosf(ang, s, c);
 }
 
 // device error word: first int32 of every workspace header

@@ -52,6 +52,7 @@ struct RowdotArgs {
     // EPI_QKV
     int S, Hq, Hkv, D;
     float rope_theta;
+    double rope_base;  // theta^(-2/D), set by the host when rope_theta > 0
     int64_t L_max;
     const int32_t* seqlens;
     bf16_t *k_cache, *v_cache, *k_out, *v_out;

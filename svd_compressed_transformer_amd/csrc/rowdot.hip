@@ -176,7 +176,7 @@ __device__ __forceinline__ void rowdot_epilogue(const RowdotArgs& a, const Rowdo
                 float y1 = x1, y2 = x2;
                 if (a.rope_theta > 0.f) {
                     float c, sn;
-                    rope_cs(p, i, a.D, a.rope_theta, &c, &sn);
+                    rope_cs(p, i, a.rope_base, &c, &sn);
                     y1 = x1 * c - x2 * sn;
                     y2 = x2 * c + x1 * sn;
                 }
