@@ -69,7 +69,7 @@ extern "C" {
 
 typedef struct ihipStream_t* fsvd_stream_t; /* a hipStream_t */
 
-#define FSVD_ABI_VERSION 3
+#define FSVD_ABI_VERSION 4
 
 typedef enum {
     FSVD_OK = 0,
@@ -223,6 +223,26 @@ fsvd_status_t fsvd_decode_attn_lowrank_kv(const void* q, const void* zk_cache, c
                                           int64_t Hq, int64_t Hkv, int64_t D, float rope_theta,
                                           float softmax_scale, int causal, void* out, fsvd_dtype_t dtype,
                                           void* ws, size_t ws_bytes, fsvd_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Factorised attention  [V1] [V15-M2]
+ * Attention of S tokens per sequence among themselves with the Q, K and V tiles rebuilt on chip
+ * from the rank-r activations, so the full-sequence q, k and v are never written:
+ *   q[b, s, h] = RoPE(z_q[b, s] . Vt_q[h*D .. h*D+D-1]^T, position s)   (k likewise, kv head g),
+ *   v[b, s, g] = z_v[b, s] . Vt_v[g*D .. g*D+D-1]^T,
+ *   o[b, s, h] = sum_{j < n} softmax_j(scale * q[b, s, h] . k[b, j, g]) v[b, j, g],
+ * with g = floor(h * Hkv / Hq) and n = s + 1 (causal) or S.  Each key tile is rebuilt once per
+ * query tile that reads it (the recomputation that replaces materialising K and V).
+ * zq, zk, zv [B * S, ldz] bf16 (row b * S + s; they may be column ranges of one packed z buffer,
+ * 16-byte aligned); Vt_q [Hq*D, r_q], Vt_k [Hkv*D, r_k], Vt_v [Hkv*D, r_v] (stored ranks, multiples
+ * of 8); out [B, S, Hq, D].  rope_theta 0 -> no RoPE; softmax_scale 0 -> 1/sqrt(D).  D 64 or 128,
+ * Hq / Hkv in {1, 2, 4, 8}.  No workspace.  bf16 only.
+ * ------------------------------------------------------------------------------------------ */
+fsvd_status_t fsvd_attn_factorized(const void* zq, const void* zk, const void* zv, int64_t ldz, const void* Vt_q,
+                                   int64_t r_q, const void* Vt_k, int64_t r_k, const void* Vt_v, int64_t r_v,
+                                   int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D, float rope_theta,
+                                   float softmax_scale, int causal, void* out, fsvd_dtype_t dtype,
+                                   fsvd_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * Swift-SVD factor production  [SWIFT-2A]

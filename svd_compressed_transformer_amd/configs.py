@@ -20,6 +20,11 @@ One JSON line per measurement on stdout:
 - swift_covariance_4096: one Swift-SVD calibration batch at the Llama-7B projection width
   (d_in = d_out = 4096, 4096 tokens): Y^T = W^T X^T and C += Y^T Y (upper triangle) on the matrix
   cores; TFLOP/s of the algorithmic flops (the product and the symmetric half of the covariance).
+- attn_factorized_bert / attn_factorized_llama7b_s2048: attention with Q/K/V rebuilt on chip from
+  the rank-r activations (nothing of q, k, v written) against the dense attention over
+  materialised q, K, V: BERT-Base encoder (8 x 512, 12 x 64, rank 384, no mask) and a causal
+  Llama-7B prefill of one 2048-token sequence (32 x 128, rank 1640, RoPE); the bytes of q, k, v the
+  factorised form never writes.
 - attn_lowrank_history_llama7b_b{1,4}: the decode attention of a Llama-7B-shaped layer over a
   2048-token history, from the dense KV cache against the layout the dense cache replaces
   (rank-1638 rows z_k, z_v cached per token, K and V rebuilt from them every step, then the same
@@ -296,6 +301,42 @@ def run_attn_history(B, history, dev, stream, copies=4):
     return res
 
 
+# ----------------------------------------------------------------------------- factorised attention
+
+
+def run_attn_factorized(name, B, S, H, D, r, theta, causal, dev, stream):
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(8)
+    bf = torch.bfloat16
+    M = B * S
+    z = torch.randn((M, 3 * r), generator=gen, device=dev).to(bf)  # packed [z_q | z_k | z_v]
+    Vq, Vk, Vv = ((torch.randn((H * D, r), generator=gen, device=dev) / math.sqrt(r)).to(bf) for _ in range(3))
+    out = torch.empty((B, S, H, D), dtype=bf, device=dev)
+    # the materialised operands of the dense path: q [B, S, H, D] and the K/V cache rows
+    q = torch.randn((B, S, H, D), generator=gen, device=dev).to(bf)
+    kc = torch.randn((B, S, H, D), generator=gen, device=dev).to(bf)
+    vc = torch.randn((B, S, H, D), generator=gen, device=dev).to(bf)
+    sl = torch.zeros(B, dtype=torch.int32, device=dev)
+    ws = fsvd.workspace(fsvd.fsvd_decode_attn_dense_kv_ws(B, S, H, H, D, S), device=dev)
+
+    def fact():
+        fsvd.fsvd_attn_factorized(z, z[:, r:], z[:, 2 * r:], 3 * r, Vq, r, Vk, r, Vv, r, B, S, H, H, D, theta, 0.0,
+                                  int(causal), out, fsvd.FSVD_BF16, stream)
+
+    def dense():
+        fsvd.fsvd_decode_attn_dense_kv(q, kc, vc, S, sl, B, S, H, H, D, 0.0, int(causal), out, fsvd.FSVD_BF16, ws,
+                                       ws.numel(), stream)
+
+    t_f = timed_median(fact, stream)
+    t_d = timed_median(dense, stream)
+    qkv_bytes = 3 * M * H * D * 2
+    return {"config": name, "batch": B, "seq": S, "heads": H, "head_dim": D, "rank": r, "causal": causal,
+            "factorized_ms": round(t_f, 4), "dense_attention_ms": round(t_d, 4),
+            "qkv_bytes_not_written": int(qkv_bytes),
+            "note": "factorized = Q/K/V rebuilt from z inside the attention; dense = attention over materialised "
+                    "q, K, V (their phase-2 products are not in dense_attention_ms)"}
+
+
 # ----------------------------------------------------------------------------- Swift-SVD covariance
 
 
@@ -337,6 +378,11 @@ def main():
                  lambda: run_decode_stack("decode_llama3_8b_gqa_b32", I.CFG4, dict(I.CFG4.ranks), I.CFG4_BATCH,
                                           I.CFG4_KV_LEN, 4, dev, stream)))
     runs.append(("swift_covariance_4096", lambda: run_swift_covariance(dev, stream)))
+    runs.append(("attn_factorized_bert", lambda: run_attn_factorized("attn_factorized_bert", 8, 512, 12, 64, 384, 0.0,
+                                                                     False, dev, stream)))
+    runs.append(("attn_factorized_llama7b_s2048",
+                 lambda: run_attn_factorized("attn_factorized_llama7b_s2048", 1, 2048, 32, 128, 1640, 1e4, True, dev,
+                                             stream)))
     for B in (1, 4):
         runs.append((f"attn_lowrank_history_llama7b_b{B}", lambda B=B: run_attn_history(B, 2048, dev, stream)))
     only = set(filter(None, args.only.split(",")))

@@ -12,18 +12,11 @@
 //
 // Source: dense-KV attention over a contiguous cache ("FlashSVD v1.5" explainer, Methodology 2);
 // prefill attention on the full sequence (same page, Methodology 2, prefill paragraph).
-#include "kernels.h"
+#include "attention_tile.h"
 
 namespace fsvd {
 
 namespace {
-
-typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNeg = -1.0e30f;
-constexpr int BQ = 64, BKV = 64;
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_prefill_mfma(const AttnArgs a) {
@@ -128,65 +121,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(const AttnArgs a) {
         __syncthreads();
         if (j0 + BKV < kend) prefetch(j0 + BKV);
 
-        // S^T blocks: lane holds keys j0 + kb*16 + 4*lg + i for query s_lane
-        f32x4 s[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int key = kb * 16 + li;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const bf16x8_v kf = __builtin_bit_cast(bf16x8_v, Ks[key * KCH + ((t * 4 + lg) ^ (key & KSW))]);
-                s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[t], s[kb], 0, 0, 0);
-            }
-        }
-        float tmax = kNeg;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t j = j0 + kb * 16 + 4 * lg + i;
-                const float v = j < n_lane ? s[kb][i] * sc : kNeg;
-                s[kb][i] = v;
-                tmax = fmaxf(tmax, v);
-            }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float mn = fmaxf(m, tmax);
-        const float alpha = exp2f(m - mn);
-        float psum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = s[kb][i] > 0.5f * kNeg ? exp2f(s[kb][i] - mn) : 0.f;
-                s[kb][i] = p;
-                psum += p;
-            }
-        l = l * alpha + psum;
-        m = mn;
-#pragma unroll
-        for (int i = 0; i < ND; ++i) o[i] *= alpha;
-
-        // O^T += V^T . P^T over two 32-key halves
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            u32x4 pw;
-            pw.x = pack_bf2(s[2 * c][0], s[2 * c][1]);
-            pw.y = pack_bf2(s[2 * c][2], s[2 * c][3]);
-            pw.z = pack_bf2(s[2 * c + 1][0], s[2 * c + 1][1]);
-            pw.w = pack_bf2(s[2 * c + 1][2], s[2 * c + 1][3]);
-            const bf16x8_v pf = __builtin_bit_cast(bf16x8_v, pw);
-            const int kc0 = 8 * c + lg, kc1 = 8 * c + 4 + lg;
-#pragma unroll
-            for (int db = 0; db < ND; ++db) {
-                const int d = db * 16 + li;
-                const uint2 lo = Vts[d * 16 + (kc0 ^ (d & 15))];
-                const uint2 hi = Vts[d * 16 + (kc1 ^ (d & 15))];
-                const bf16x8_v vf = __builtin_bit_cast(bf16x8_v, u32x4{lo.x, lo.y, hi.x, hi.y});
-                o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[db], 0, 0, 0);
-            }
-        }
+        attn_tile<D>(Ks, Vts, qf, j0, n_lane, sc, m, l, o, li, lg);
     }
 
     float lt = l;

@@ -1,0 +1,89 @@
+// Shared MFMA flash-attention tile step (gfx950, v_mfma_f32_16x16x32_bf16): used by the prefill
+// attention over the dense cache and by the factorised attention that rebuilds its tiles on chip.
+#pragma once
+
+#include "kernels.h"
+
+namespace fsvd {
+namespace {
+
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNeg = -1.0e30f;
+constexpr int BQ = 64, BKV = 64;  // queries per workgroup (16 per wave), keys per tile
+
+// One key tile of the MFMA flash attention: the 64 keys j0 .. j0 + 63 staged in LDS (Ks: K rows
+// with XOR-swizzled 16-byte chunks; Vts: V transposed, 4 keys per uint2 per head dimension)
+// against this wave's 16 queries (qf: the B operand, lane (li, lg) holding q[query li][t*32 +
+// lg*8 .. +7]); keys at or past n_lane are masked.  Updates the running max m, sum l and the
+// O^T accumulators o (lane (li, lg): dims db*16 + 4*lg + 0..3 of query li).
+template <int D>
+__device__ __forceinline__ void attn_tile(const u32x4* Ks, const uint2* Vts, const bf16x8_v (&qf)[D / 32], int64_t j0,
+                                          int64_t n_lane, float sc, float& m, float& l, f32x4 (&o)[D / 16], int li,
+                                          int lg) {
+    constexpr int NT = D / 32, ND = D / 16, KCH = D / 8, KSW = KCH - 1;
+    // S^T blocks: lane holds keys j0 + kb*16 + 4*lg + i for query s_lane
+    f32x4 s[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int key = kb * 16 + li;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const bf16x8_v kf = __builtin_bit_cast(bf16x8_v, Ks[key * KCH + ((t * 4 + lg) ^ (key & KSW))]);
+            s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[t], s[kb], 0, 0, 0);
+        }
+    }
+    float tmax = kNeg;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t j = j0 + kb * 16 + 4 * lg + i;
+            const float v = j < n_lane ? s[kb][i] * sc : kNeg;
+            s[kb][i] = v;
+            tmax = fmaxf(tmax, v);
+        }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mn = fmaxf(m, tmax);
+    const float alpha = exp2f(m - mn);
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float p = s[kb][i] > 0.5f * kNeg ? exp2f(s[kb][i] - mn) : 0.f;
+            s[kb][i] = p;
+            psum += p;
+        }
+    l = l * alpha + psum;
+    m = mn;
+#pragma unroll
+    for (int i = 0; i < ND; ++i) o[i] *= alpha;
+
+    // O^T += V^T . P^T over two 32-key halves
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        u32x4 pw;
+        pw.x = pack_bf2(s[2 * c][0], s[2 * c][1]);
+        pw.y = pack_bf2(s[2 * c][2], s[2 * c][3]);
+        pw.z = pack_bf2(s[2 * c + 1][0], s[2 * c + 1][1]);
+        pw.w = pack_bf2(s[2 * c + 1][2], s[2 * c + 1][3]);
+        const bf16x8_v pf = __builtin_bit_cast(bf16x8_v, pw);
+        const int kc0 = 8 * c + lg, kc1 = 8 * c + 4 + lg;
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+            const int d = db * 16 + li;
+            const uint2 lo = Vts[d * 16 + (kc0 ^ (d & 15))];
+            const uint2 hi = Vts[d * 16 + (kc1 ^ (d & 15))];
+            const bf16x8_v vf = __builtin_bit_cast(bf16x8_v, u32x4{lo.x, lo.y, hi.x, hi.y});
+            o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[db], 0, 0, 0);
+        }
+    }
+}
+
+}  // namespace
+}  // namespace fsvd

@@ -664,6 +664,35 @@ fsvd_status_t fsvd_decode_attn_lowrank_kv(const void* q, const void* zk_cache, c
                         causal, out, part, ns, (int*)ws, st);
 }
 
+fsvd_status_t fsvd_attn_factorized(const void* zq, const void* zk, const void* zv, int64_t ldz, const void* Vt_q,
+                                   int64_t r_q, const void* Vt_k, int64_t r_k, const void* Vt_v, int64_t r_v,
+                                   int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D, float rope_theta,
+                                   float softmax_scale, int causal, void* out, fsvd_dtype_t dtype,
+                                   fsvd_stream_t stream) {
+    TRY(need_dtype(dtype, false));
+    TRY(need_dim(B, "B")); TRY(need_dim(S, "S")); TRY(need_dim(Hq, "Hq")); TRY(need_dim(Hkv, "Hkv"));
+    TRY(need_dim(D, "D")); TRY(need_dim(r_q, "r_q")); TRY(need_dim(r_k, "r_k")); TRY(need_dim(r_v, "r_v"));
+    TRY(check_attn_shape(Hq, Hkv, D));
+    TRY(need_vec(r_q, dtype, "r_q")); TRY(need_vec(r_k, dtype, "r_k")); TRY(need_vec(r_v, dtype, "r_v"));
+    TRY(need_ld(ldz, std::max(r_q, std::max(r_k, r_v)), dtype, "ldz"));
+    if (B * S > (int64_t)1 << 30) return fail(FSVD_ERR_UNSUPPORTED, "B * S too large");
+    TRY(need_ptr(zq, "zq")); TRY(need_ptr(zk, "zk")); TRY(need_ptr(zv, "zv"));
+    TRY(need_ptr(Vt_q, "Vt_q")); TRY(need_ptr(Vt_k, "Vt_k")); TRY(need_ptr(Vt_v, "Vt_v")); TRY(need_ptr(out, "out"));
+    if (softmax_scale < 0.f) return fail(FSVD_ERR_INVALID_ARG, "softmax_scale must be >= 0");
+    if (rope_theta < 0.f) return fail(FSVD_ERR_INVALID_ARG, "rope_theta must be >= 0");
+    FactAttnArgs a{};
+    a.zq = (const bf16_t*)zq; a.zk = (const bf16_t*)zk; a.zv = (const bf16_t*)zv; a.ldz = ldz;
+    a.Vq = (const bf16_t*)Vt_q; a.Vk = (const bf16_t*)Vt_k; a.Vv = (const bf16_t*)Vt_v;
+    a.rq = (int)r_q; a.rk = (int)r_k; a.rv = (int)r_v;
+    a.B = (int)B; a.S = (int)S; a.Hq = (int)Hq; a.Hkv = (int)Hkv; a.D = (int)D;
+    a.rope_theta = rope_theta;
+    a.rope_base = rope_theta > 0.f ? std::pow((double)rope_theta, -2.0 / (double)D) : 0.0;
+    a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+    a.causal = causal;
+    a.out = (bf16_t*)out;
+    return launch_attn_factorized(a, (hipStream_t)stream);
+}
+
 size_t fsvd_swift_covariance_ws(int64_t T, int64_t d_in, int64_t d_out) {
     (void)d_in;
     if (T <= 0 || d_out <= 0) return kWsHeader;

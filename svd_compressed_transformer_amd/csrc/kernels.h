@@ -83,6 +83,20 @@ struct AttnArgs {
     float* part;       // decode partials [B, Hq, nsplit, D + 2]
     int* err;
 };
+// factorised attention: S tokens per sequence among themselves, Q/K/V rebuilt from z on chip
+struct FactAttnArgs {
+    const bf16_t *zq, *zk, *zv;  // [B * S, ldz] rank activations (may be column ranges of one buffer)
+    int64_t ldz;
+    const bf16_t *Vq, *Vk, *Vv;  // [Hq * D, rq], [Hkv * D, rk], [Hkv * D, rv]
+    int rq, rk, rv;
+    int B, S, Hq, Hkv, D;
+    float rope_theta;            // 0: no RoPE
+    double rope_base;            // theta^(-2/D)
+    float scale;
+    int causal;
+    bf16_t* out;                 // [B, S, Hq, D]
+};
+fsvd_status_t launch_attn_factorized(const FactAttnArgs& a, hipStream_t st);
 size_t attn_decode_ws_bytes(int B, int Hq, int D, int nsplit);
 int attn_default_splits(int B, int Hkv, int64_t L_max);
 fsvd_status_t launch_attn_decode(const AttnArgs& a, hipStream_t st);

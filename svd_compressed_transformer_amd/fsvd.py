@@ -63,6 +63,8 @@ _SIGS = {
     "fsvd_decode_attn_lowrank_kv_ws": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
     "fsvd_decode_attn_lowrank_kv": (C.c_int, [_vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64,
                                               _i64, _i64, _f32, _f32, C.c_int, _vp, C.c_int, _vp, _sz, _vp]),
+    "fsvd_attn_factorized": (C.c_int, [_vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
+                                       _i64, _f32, _f32, C.c_int, _vp, C.c_int, _vp]),
     "fsvd_swift_covariance_ws": (_sz, [_i64, _i64, _i64]),
     "fsvd_swift_covariance": (C.c_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
     "fsvd_swift_factors_ws": (_sz, [_i64, _i64]),
@@ -214,6 +216,12 @@ def fsvd_decode_attn_lowrank_kv(q, zk_cache, zv_cache, ldz, Vt_k, r_k, Vt_v, r_v
     _check(lib().fsvd_decode_attn_lowrank_kv(_p(q), _p(zk_cache), _p(zv_cache), ldz, _p(Vt_k), r_k, _p(Vt_v), r_v,
                                              L_max, _p(cache_seqlens), B, Sq, Hq, Hkv, D, rope_theta, softmax_scale,
                                              int(causal), _p(out), dtype, _p(ws), ws_bytes, _s(stream)))
+
+
+def fsvd_attn_factorized(zq, zk, zv, ldz, Vt_q, r_q, Vt_k, r_k, Vt_v, r_v, B, S, Hq, Hkv, D, rope_theta, softmax_scale,
+                         causal, out, dtype, stream=None):
+    _check(lib().fsvd_attn_factorized(_p(zq), _p(zk), _p(zv), ldz, _p(Vt_q), r_q, _p(Vt_k), r_k, _p(Vt_v), r_v, B, S,
+                                      Hq, Hkv, D, rope_theta, softmax_scale, int(causal), _p(out), dtype, _s(stream)))
 
 
 def fsvd_swift_covariance_ws(T, d_in, d_out) -> int:

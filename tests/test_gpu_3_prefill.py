@@ -175,3 +175,61 @@ def test_encoder_layer_small():
     p = I.make_encoder_layer(cfg, B=B, S=S, seed=5)
     y = encoder_forward(cfg, p, B, S)
     assert rel(y, O.encoder_layer(p["x"], p, cfg)) <= BF16_TOL
+
+
+# ----------------------------------------------------------------------------- factorised attention
+
+
+def _factorized_case(B, S, Hq, Hkv, D, rq, rk, rv, theta, causal, packed, seed):
+    rng = np.random.default_rng(seed)
+    ldz = rq + rk + rv if packed else max(rq, rk, rv) + 8
+    z = [I.round_bf16(rng.standard_normal((B * S, ldz))) for _ in range(1 if packed else 3)]
+    Vq = I.round_bf16(rng.standard_normal((Hq * D, rq)) / np.sqrt(rq))
+    Vk = I.round_bf16(rng.standard_normal((Hkv * D, rk)) / np.sqrt(rk))
+    Vv = I.round_bf16(rng.standard_normal((Hkv * D, rv)) / np.sqrt(rv))
+    if packed:
+        zq, zk, zv = z[0][:, :rq], z[0][:, rq:rq + rk], z[0][:, rq + rk:]
+    else:
+        zq, zk, zv = z[0][:, :rq], z[1][:, :rk], z[2][:, :rv]
+    dz = [to_dev(a) for a in z]
+    if packed:
+        base = dz[0]
+        ptrs = (base, base[:, rq:], base[:, rq + rk:])
+    else:
+        ptrs = tuple(dz)
+    out = torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device="cuda")
+    fsvd.fsvd_attn_factorized(ptrs[0], ptrs[1], ptrs[2], ldz, to_dev(Vq), rq, to_dev(Vk), rk, to_dev(Vv), rv, B, S, Hq,
+                              Hkv, D, theta, 0.0, causal, out, fsvd.FSVD_BF16)
+    torch.cuda.synchronize()
+    # oracle: the same products written out, then attention over the rebuilt K/V
+    q = (np.asarray(zq, dtype=np.float64) @ Vq.T).reshape(B, S, Hq, D)
+    if theta:
+        q = O.rope(q, np.arange(S)[None, :, None], theta)
+    K, V = O.lowrank_history_kv(np.asarray(zk).reshape(B, S, rk), np.asarray(zv).reshape(B, S, rv), Vk, Vv, Hkv, D,
+                                theta)
+    ref = O.attention(q, K, V, np.zeros(B, dtype=np.int64), causal=causal)
+    return from_dev(out), ref
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,rq,rk,rv,theta,causal,packed", [
+    (2, 100, 4, 4, 64, 40, 40, 40, 0.0, False, False),      # encoder: two query tiles, ragged ranks
+    (1, 130, 8, 2, 128, 48, 24, 16, 1e4, True, True),       # causal GQA with RoPE, packed z columns
+    (3, 64, 4, 1, 64, 32, 8, 64, 5e5, True, False),         # one tile, GQA 4:1
+])
+def test_attention_factorized(B, S, Hq, Hkv, D, rq, rk, rv, theta, causal, packed):
+    """Q/K/V rebuilt on chip from z: against the oracle's products, RoPE and attention."""
+    say("factorised attention", B, S, Hq, Hkv, D, rq, rk, rv, theta, causal, packed)
+    o, ref = _factorized_case(B, S, Hq, Hkv, D, rq, rk, rv, theta, causal, packed, seed=B * S)
+    err = rel(o, ref)
+    say(f"  err {err:.2e}")
+    assert np.all(np.isfinite(o)) and err <= BF16_TOL
+
+
+@pytest.mark.slow
+def test_attention_factorized_bert_base():
+    """The BERT-Base encoder shape: batch 8 x 512, 12 heads x 64, rank 384, no mask."""
+    say("factorised attention, BERT-Base shape")
+    o, ref = _factorized_case(8, 512, 12, 12, 64, 384, 384, 384, 0.0, False, True, seed=5)
+    err = rel(o, ref)
+    say(f"  err {err:.2e}")
+    assert err <= BF16_TOL
