@@ -49,6 +49,11 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(const AttnArgs a) {
     int64_t n_lane = a.causal ? base + s_lane + 1 : base + a.Sq;
     if (n_lane > a.L_max) n_lane = a.L_max;
     if (s_lane >= a.Sq) n_lane = 0;
+    // fewest keys any query of this wave sees (tiles below it need no mask)
+    const int first = qt * BQ + wave * 16;
+    int64_t n_min = a.causal ? base + first + 1 : base + a.Sq;
+    if (n_min > a.L_max) n_min = a.L_max;
+    if (first + 15 >= a.Sq) n_min = 0;
 
     // Q as the B operand: lane (li, lg) holds q[s_lane][t*32 + lg*8 .. +7]
     bf16x8_v qf[NT];
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(const AttnArgs a) {
         __syncthreads();
         if (j0 + BKV < kend) prefetch(j0 + BKV);
 
-        attn_tile<D>(Ks, Vts, qf, j0, n_lane, sc, m, l, o, li, lg);
+        attn_tile<D>(Ks, Vts, qf, (int)j0, (int)n_lane, (int)n_min, sc, m, l, o, li, lg);
     }
 
     float lt = l;
@@ -145,6 +150,7 @@ fsvd_status_t launch_attn_prefill(const AttnArgs& a, hipStream_t st) {
     const int64_t grid = (int64_t)n_qt * a.B * a.Hq;
     if (grid <= 0) return FSVD_OK;
     if (grid > 0x7fffffff) return fail(FSVD_ERR_UNSUPPORTED, "attention grid too large");
+    if (a.L_max > 0x7fffffff - 64) return fail(FSVD_ERR_UNSUPPORTED, "cache length %lld too large", (long long)a.L_max);
     if (a.D == 128) attn_prefill_mfma<128><<<(unsigned)grid, 256, 0, st>>>(a);
     else if (a.D == 64) attn_prefill_mfma<64><<<(unsigned)grid, 256, 0, st>>>(a);
     else return fail(FSVD_ERR_UNSUPPORTED, "head dim %d not in {64,128}", a.D);

@@ -17,12 +17,13 @@ constexpr int BQ = 64, BKV = 64;  // queries per workgroup (16 per wave), keys p
 // One key tile of the MFMA flash attention: the 64 keys j0 .. j0 + 63 staged in LDS (Ks: K rows
 // with XOR-swizzled 16-byte chunks; Vts: V transposed, 4 keys per uint2 per head dimension)
 // against this wave's 16 queries (qf: the B operand, lane (li, lg) holding q[query li][t*32 +
-// lg*8 .. +7]); keys at or past n_lane are masked.  Updates the running max m, sum l and the
-// O^T accumulators o (lane (li, lg): dims db*16 + 4*lg + 0..3 of query li).
-template <int D>
-__device__ __forceinline__ void attn_tile(const u32x4* Ks, const uint2* Vts, const bf16x8_v (&qf)[D / 32], int64_t j0,
-                                          int64_t n_lane, float sc, float& m, float& l, f32x4 (&o)[D / 16], int li,
-                                          int lg) {
+// lg*8 .. +7]); with MASK, keys at or past n_lane are masked (without it every key of the tile is
+// below every n_lane of the wave).  Updates the running max m, sum l and the O^T accumulators o
+// (lane (li, lg): dims db*16 + 4*lg + 0..3 of query li).  exp2 is the hardware v_exp_f32.
+template <int D, bool MASK>
+__device__ __forceinline__ void attn_tile_m(const u32x4* Ks, const uint2* Vts, const bf16x8_v (&qf)[D / 32], int j0,
+                                            int n_lane, float sc, float& m, float& l, f32x4 (&o)[D / 16], int li,
+                                            int lg) {
     constexpr int NT = D / 32, ND = D / 16, KCH = D / 8, KSW = KCH - 1;
     // S^T blocks: lane holds keys j0 + kb*16 + 4*lg + i for query s_lane
     f32x4 s[4];
@@ -41,21 +42,22 @@ __device__ __forceinline__ void attn_tile(const u32x4* Ks, const uint2* Vts, con
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t j = j0 + kb * 16 + 4 * lg + i;
-            const float v = j < n_lane ? s[kb][i] * sc : kNeg;
+            float v = s[kb][i] * sc;
+            if constexpr (MASK) v = j0 + kb * 16 + 4 * lg + i < n_lane ? v : kNeg;
             s[kb][i] = v;
             tmax = fmaxf(tmax, v);
         }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float mn = fmaxf(m, tmax);
-    const float alpha = exp2f(m - mn);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float p = s[kb][i] > 0.5f * kNeg ? exp2f(s[kb][i] - mn) : 0.f;
+            float p = __builtin_amdgcn_exp2f(s[kb][i] - mn);
+            if constexpr (MASK) p = s[kb][i] > 0.5f * kNeg ? p : 0.f;
             s[kb][i] = p;
             psum += p;
         }
@@ -83,6 +85,16 @@ __device__ __forceinline__ void attn_tile(const u32x4* Ks, const uint2* Vts, con
             o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[db], 0, 0, 0);
         }
     }
+}
+
+// The tile step for a wave whose queries all see at least n_min keys: the mask is applied only to
+// tiles that reach n_min.
+template <int D>
+__device__ __forceinline__ void attn_tile(const u32x4* Ks, const uint2* Vts, const bf16x8_v (&qf)[D / 32], int j0,
+                                          int n_lane, int n_min, float sc, float& m, float& l, f32x4 (&o)[D / 16],
+                                          int li, int lg) {
+    if (j0 + BKV <= n_min) attn_tile_m<D, false>(Ks, Vts, qf, j0, n_lane, sc, m, l, o, li, lg);
+    else attn_tile_m<D, true>(Ks, Vts, qf, j0, n_lane, sc, m, l, o, li, lg);
 }
 
 }  // namespace

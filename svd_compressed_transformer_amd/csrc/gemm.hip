@@ -85,29 +85,6 @@ __device__ __forceinline__ void zero_k_tail(u32x4* dst, int k0, int K, int tid) 
     }
 }
 
-// s_waitcnt on the vector-memory counter only: vmcnt in bits [3:0] and [15:14], expcnt (bits 6:4)
-// and lgkmcnt (bits 11:8) left at their maxima so they do not wait
-#define FSVD_VMCNT(n) (0x0F70 | ((n) & 0xF) | ((((n) >> 4) & 3) << 14))
-__device__ __forceinline__ void wait_vm(int n) {
-    // wait until at most n vector-memory operations of this wave are outstanding (n rounded down)
-    if (n >= 24) __builtin_amdgcn_s_waitcnt(FSVD_VMCNT(24));
-    else if (n >= 16) __builtin_amdgcn_s_waitcnt(FSVD_VMCNT(16));
-    else if (n >= 12) __builtin_amdgcn_s_waitcnt(FSVD_VMCNT(12));
-    else if (n >= 8) __builtin_amdgcn_s_waitcnt(FSVD_VMCNT(8));
-    else if (n >= 6) __builtin_amdgcn_s_waitcnt(FSVD_VMCNT(6));
-    else __builtin_amdgcn_s_waitcnt(FSVD_VMCNT(0));
-}
-
-// Workgroup barrier that waits for this wave's LDS operations only.  __syncthreads() would also
-// drain every outstanding global load (vmcnt(0)), i.e. the prefetches of later stages, which is
-// exactly what the pipeline must keep in flight; stage arrival is ordered by wait_vm() instead.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt unchanged
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 // Instruction order for one pipeline step of NM MFMAs: one memory instruction after each of the
 // first MFMAs, the NR LDS reads (fragments of the next k step) first so they land well before
 // the step ends, then the NG global loads, then the remaining MFMAs.

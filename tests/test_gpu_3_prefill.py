@@ -215,6 +215,9 @@ def _factorized_case(B, S, Hq, Hkv, D, rq, rk, rv, theta, causal, packed, seed):
     (2, 100, 4, 4, 64, 40, 40, 40, 0.0, False, False),      # encoder: two query tiles, ragged ranks
     (1, 130, 8, 2, 128, 48, 24, 16, 1e4, True, True),       # causal GQA with RoPE, packed z columns
     (3, 64, 4, 1, 64, 32, 8, 64, 5e5, True, False),         # one tile, GQA 4:1
+    (1, 200, 4, 2, 128, 136, 72, 200, 1e4, True, False),    # several rank chunks, ragged last chunk, rk != rv
+    (4, 260, 32, 8, 64, 136, 200, 72, 1e4, True, True),     # 256-query workgroups (D = 64, enough of them)
+    (2, 300, 6, 6, 64, 264, 264, 264, 0.0, False, True),    # encoder, 128-query workgroups, ragged tiles
 ])
 def test_attention_factorized(B, S, Hq, Hkv, D, rq, rk, rv, theta, causal, packed):
     """Q/K/V rebuilt on chip from z: against the oracle's products, RoPE and attention."""
