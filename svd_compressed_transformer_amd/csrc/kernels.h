@@ -63,7 +63,7 @@ struct RowdotArgs {
 };
 
 // Launch one row-dot kernel.  dtype FSVD_BF16 (all epilogues) or FSVD_F32 (EPI_Z, EPI_LINEAR).
-// bf16 launches with 9..32 activation rows run the products on the matrix cores.
+// bf16 launches with 5..32 activation rows run the products on the matrix cores.
 fsvd_status_t launch_rowdot(const RowdotArgs& a, int epi, fsvd_dtype_t dtype, hipStream_t st);
 // Helper filling seg.blk_begin / units_per_blk and returning the total grid size.
 int rowdot_plan(RowdotArgs& a, int epi, fsvd_dtype_t dtype);

@@ -381,16 +381,16 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
                             tid, 64 * a.waves, val, [&](int g, int m) { return val(g, 0, kR, m); });
 }
 
-// Skinny-MFMA variant for 9..32 activation rows (bf16).  Past about 8 rows the row-dot's dot
+// Skinny-MFMA variant for 5..32 activation rows (bf16).  Past about 4 rows the row-dot's dot
 // products, which grow with the number of activation rows while the factor bytes do not, make
 // the kernel vector-ALU bound (measured on MI355X: the instruction count and the time grow with
 // the batch).  Here a wave owns a tile of 16 factor rows and its products run on the matrix
 // cores as v_mfma_f32_16x16x32_bf16: the B operand is 16 factor rows x 32 k (lane l holds 8
-// consecutive k of row l % 16 at k group l / 16, so one load instruction reads 64 contiguous bytes
-// of each row), the A operand 16 activation rows x 32 k with the same k groups (MB = 2 tiles for
-// 17..32 rows); C[m][row] accumulates in fp32.  The factor stream, the k split over waves, the
-// RMSNorm statistics and the epilogues are those of the row-dot; the partial tiles of the waves
-// that split k are summed from LDS.
+// consecutive k of row l % 16 at k group l / 16), read from a wave-private LDS stage that the
+// pass fills with row-contiguous direct loads; the A operand is 16 activation rows x 32 k with
+// the same k groups (MB = 2 tiles for 17..32 rows); C[m][row] accumulates in fp32.  The k split
+// over waves, the RMSNorm statistics and the epilogues are those of the row-dot; the partial
+// tiles of the waves that split k are summed from LDS.
 typedef __bf16 bf16x8_m __attribute__((ext_vector_type(8)));
 typedef float f32x4_m __attribute__((ext_vector_type(4)));
 constexpr int kMfmaRows = 16;  // factor rows per wave tile
@@ -551,9 +551,16 @@ __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
     for (int s0 = 0; s0 < nsteps; s0 += U) pass(std::integral_constant<int, U>(), s0);
 
     // C tile of this wave: lane holds C[m = 16 mb + 4 kq + e][row rj]; the k-split waves of a unit
-    // group are summed from LDS.  Sums of squares: over the 4 k groups of an activation row.
+    // group are summed from LDS.  Sums of squares: over the 4 k groups of an activation row.  The
+    // combine arrays reuse the stage buffers once every wave is past its last pass.
+#if FSVD_RD_MFMA_LDS
+    __syncthreads();
+    float (*red)[32][kMfmaRows] = reinterpret_cast<float (*)[32][kMfmaRows]>(rd_stage);
+    float (*red_ss)[32] = reinterpret_cast<float (*)[32]>(reinterpret_cast<float*>(rd_stage) + kMaxWaves * 32 * kMfmaRows);
+#else
     __shared__ float red[kMaxWaves][32][kMfmaRows];
     __shared__ float red_ss[kMaxWaves][32];
+#endif
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -607,17 +614,15 @@ fsvd_status_t launch_b(const RowdotArgs& a, int grid, hipStream_t st) {
 
 namespace {
 
-// bf16 launches of 9..32 activation rows go to the matrix cores, except reductions longer than
-// 8192 over at most 16 rows, where the 16-row tiles leave too few waves (measured on MI355X: the
-// down projection's phase 1, K = 11008, is faster on v_dot2 at 16 rows and even at 32).
+// bf16 launches of 5..32 activation rows go to the matrix cores.  Measured on MI355X (Llama-7B
+// layer-step over 2048 positions, factor rows staged through LDS): batch 8 159.9 us on the matrix
+// cores against 172.2 us on v_dot2 (which runs 5..8 rows as 8), batch 4 134.3 against 121.7 us.
 #ifndef FSVD_RD_MFMA_MIN_M
-#define FSVD_RD_MFMA_MIN_M 9
+#define FSVD_RD_MFMA_MIN_M 5
 #endif
 bool use_mfma(const RowdotArgs& a, int epi, fsvd_dtype_t dtype) {
-    if (dtype != FSVD_BF16 || a.M < FSVD_RD_MFMA_MIN_M) return false;
-    int kmax = 0;
-    for (int i = 0; i < a.nseg; ++i) kmax = std::max(kmax, std::max(a.seg[i].K, epi == EPI_SWIGLU ? a.seg[i].K2 : 0));
-    return !(a.M <= 16 && kmax > 8192);
+    (void)epi;
+    return dtype == FSVD_BF16 && a.M >= FSVD_RD_MFMA_MIN_M;
 }
 
 // rows: factor rows per wave (kR for the v_dot2 kernel, 16 for the MFMA kernel)
@@ -658,8 +663,10 @@ int plan_rows(RowdotArgs& a, int epi, int rows, bool mfma) {
 
 template <int EPI>
 fsvd_status_t launch_mfma(const RowdotArgs& a, int grid, hipStream_t st) {
-    const size_t lds1 = FSVD_RD_MFMA_LDS ? (size_t)a.waves * mfma_stage_slots<1>() * 16 : 0;
-    const size_t lds2 = FSVD_RD_MFMA_LDS ? (size_t)a.waves * mfma_stage_slots<2>() * 16 : 0;
+    // the stages, or the combine arrays that reuse them, whichever is larger
+    constexpr size_t kRed = (size_t)kMaxWaves * 32 * (kMfmaRows + 1) * sizeof(float);
+    const size_t lds1 = FSVD_RD_MFMA_LDS ? std::max((size_t)a.waves * mfma_stage_slots<1>() * 16, kRed) : 0;
+    const size_t lds2 = FSVD_RD_MFMA_LDS ? std::max((size_t)a.waves * mfma_stage_slots<2>() * 16, kRed) : 0;
     static bool attr_set = false;  // the dynamic LDS limit (up to 64 KiB of stages) raised once
     if (!attr_set) {
         (void)hipFuncSetAttribute((const void*)rowdot_mfma_kernel<1, EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -109,7 +109,7 @@ def test_linear_cfg0_fp32():
 
 @pytest.mark.parametrize("M,K,r,N", [(1, 512, 64, 256), (3, 1000, 40, 1032), (7, 4096, 1640, 520),
                                      (16, 2048, 24, 3000), (32, 768, 392, 768), (5, 8, 8, 8),
-                                     # 9..32 rows run on the matrix cores: one and two 16-row tiles,
+                                     # 5..32 rows run on the matrix cores: one and two 16-row tiles,
                                      # ragged K, rank and N
                                      (9, 4096, 1640, 4096), (17, 1000, 40, 1032), (24, 11008, 1640, 520),
                                      (32, 8, 8, 8)])
