@@ -526,8 +526,6 @@ __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
         }
 #if FSVD_RD_MFMA_LDS
         wait_vm(0);  // this wave's staged rows have landed (the buffer is private: no barrier)
-#pragma unroll
-        for (int q = 0; q < NU; ++q) wv[q] = stg[rj * CPR + ((q * 4 + kq) ^ rj)];
 #endif
 #pragma unroll
         for (int q = 0; q < NU; ++q) {
@@ -540,6 +538,9 @@ __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
                         if (norm_w) x = vmulw(x, nw[q]);
                     }
                 }
+#if FSVD_RD_MFMA_LDS
+                if (mb == 0) wv[q] = stg[rj * CPR + ((q * 4 + kq) ^ rj)];  // B fragment of step q from the stage
+#endif
                 acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_m, x),
                                                                    __builtin_bit_cast(bf16x8_m, wv[q]), acc[mb], 0, 0, 0);
             }
