@@ -399,9 +399,6 @@ constexpr int kMfmaSteps = 8;  // 32-wide k steps whose loads one pass keeps in 
 // instruction reads 512 or 256 contiguous bytes of each of 2 or 4 rows) instead of loading the
 // MFMA operand layout directly (64 bytes of each of 16 rows per instruction).  Measured on MI355X
 // with a plain stream of the same bytes and waves: 4.8-5.4 TB/s against 3.0-4.4 TB/s.
-#ifndef FSVD_RD_MFMA_LDS
-#define FSVD_RD_MFMA_LDS 1
-#endif
 typedef __attribute__((address_space(3))) void lds_void_rd;
 template <int MB>
 constexpr int mfma_pass_steps() { return MB == 1 ? kMfmaSteps : kMfmaSteps / 2; }
@@ -409,7 +406,7 @@ constexpr int mfma_pass_steps() { return MB == 1 ? kMfmaSteps : kMfmaSteps / 2; 
 template <int MB>
 constexpr int mfma_stage_slots() { return kMfmaRows * mfma_pass_steps<MB>() * 4; }
 
-template <int MB, int EPI>
+template <int MB, int EPI, bool DB>
 __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
     using T = bf16_t;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -444,7 +441,6 @@ __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
     const bool valid = u < n_units;
     const char* W = reinterpret_cast<const char*>(mat ? sg.W2 : sg.W);
     const int64_t ldw = mat ? sg.ldw2 : sg.ldw;
-    const char* wrow = W + (valid ? (int64_t)n * ldw * (int64_t)sizeof(T) : 0);
     // factor row of tile row j (the staged loads give a lane rows other than its own column rj)
     auto row_ptr = [&](int j) -> const char* {
         int uj, nj;
@@ -459,7 +455,7 @@ __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
         return W + (uj < n_units ? (int64_t)nj * ldw * (int64_t)sizeof(T) : 0);
     };
     extern __shared__ u32x4 rd_stage[];
-    u32x4* stg = rd_stage + wave * mfma_stage_slots<MB>();
+    u32x4* stg = rd_stage + wave * mfma_stage_slots<MB>() * (DB ? 2 : 1);  // this wave's stage(s)
 
     constexpr int SE = 32;  // k per MFMA step
     const int kmax = (EPI == EPI_SWIGLU) ? max(sg.K, sg.K2) : sg.K;
@@ -489,46 +485,54 @@ __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
         ss[mb] = 0.f;
     }
     const int nsteps = k_hi > k_lo ? (k_hi - k_lo + SE - 1) / SE : 0;
-    auto pass = [&](auto nu_c, int s0) {
-        constexpr int NU = decltype(nu_c)::value;
-        u32x4 wv[NU], nw[NU], av[NU][MB];
-#if FSVD_RD_MFMA_LDS
-        // stage: slot s of the wave's buffer holds row j = s / CPR, chunk c = (s % CPR) ^ j of the
-        // pass (CPR = 4 NU chunks of 16 bytes per row, a power of two >= 16 > j)
-        constexpr int CPR = NU * 4, NI = kMfmaRows * CPR / 64;
-        static_assert(NU == mfma_pass_steps<MB>(), "stage sized for whole passes");
+    // Whole passes of U steps (a shorter last pass would cost one round trip per step); steps past
+    // the slice load clamped addresses (cache hits) and are zeroed by the activation mask.  The
+    // factor rows of a pass go to the wave's stage: slot s holds row j = s / CPR, chunk
+    // c = (s % CPR) ^ j of the pass (CPR = 4 U chunks of 16 bytes per row, a power of two >= 16 > j).
+    constexpr int U = mfma_pass_steps<MB>();
+    constexpr int CPR = U * 4, NI = kMfmaRows * CPR / 64, SLOTS = mfma_stage_slots<MB>();
+    const int npass = (nsteps + U - 1) / U;
+    auto stage = [&](int p, u32x4* dst) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int sl = i * 64 + lane, j = sl / CPR, c = (sl % CPR) ^ j;
-            const int k = min(k_lo + s0 * SE + c * 8, kc_max);
+            const int k = min(k_lo + p * U * SE + c * 8, kc_max);
             __builtin_amdgcn_global_load_lds((const void*)(row_ptr(j) + (int64_t)k * sizeof(T)),
-                                             (lds_void_rd*)(stg + i * 64), 16, 0, 0);
+                                             (lds_void_rd*)(dst + i * 64), 16, 0, 0);
         }
-#endif
+    };
+    if (npass > 0) stage(0, stg);
+    for (int p = 0; p < npass; ++p) {
+        const int s0 = p * U;
+        u32x4 nw[U], av[U][MB];
 #pragma unroll
-        for (int q = 0; q < NU; ++q) {
+        for (int q = 0; q < U; ++q) {
             const int k = k_lo + (s0 + q) * SE + kq * 8;
             const int64_t kc = (int64_t)min(k, kc_max) * sizeof(T);
-#if !FSVD_RD_MFMA_LDS
-            wv[q] = ldg16_stream(wrow + kc);
-#endif
             if (norm_w) nw[q] = ldg16(nwp + kc);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) av[q][mb] = ldg16(arow[mb] + kc);
         }
-        if (k_lo + (s0 + NU) * SE > k_end) {  // wave-uniform: the pass reaches past k_end
+        if (k_lo + (s0 + U) * SE > k_end) {  // wave-uniform: the pass reaches past k_end
 #pragma unroll
-            for (int q = 0; q < NU; ++q) {
+            for (int q = 0; q < U; ++q) {
                 const bool ok = k_lo + (s0 + q) * SE + kq * 8 < k_end;
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) av[q][mb] = ok ? av[q][mb] : u32x4{0u, 0u, 0u, 0u};
             }
         }
-#if FSVD_RD_MFMA_LDS
-        wait_vm(0);  // this wave's staged rows have landed (the buffer is private: no barrier)
-#endif
+        wait_vm(0);  // this pass's staged rows and activations have landed (private stage: no barrier)
+        const u32x4* cur = stg + (DB ? (p & 1) * SLOTS : 0);
+        u32x4 wv[U];
+        if constexpr (DB) {
+            // double-buffered: every fragment of this pass is read before the next pass's loads are
+            // issued into the other buffer, so no read of the stage overlaps loads in flight
 #pragma unroll
-        for (int q = 0; q < NU; ++q) {
+            for (int q = 0; q < U; ++q) wv[q] = cur[rj * CPR + ((q * 4 + kq) ^ rj)];
+            if (p + 1 < npass) stage(p + 1, stg + ((p + 1) & 1) * SLOTS);
+        }
+#pragma unroll
+        for (int q = 0; q < U; ++q) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 u32x4 x = av[q][mb];
@@ -538,30 +542,25 @@ __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
                         if (norm_w) x = vmulw(x, nw[q]);
                     }
                 }
-#if FSVD_RD_MFMA_LDS
-                if (mb == 0) wv[q] = stg[rj * CPR + ((q * 4 + kq) ^ rj)];  // B fragment of step q from the stage
-#endif
+                if constexpr (!DB) {
+                    if (mb == 0) wv[q] = cur[rj * CPR + ((q * 4 + kq) ^ rj)];  // B fragment of step q
+                }
                 acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_m, x),
                                                                    __builtin_bit_cast(bf16x8_m, wv[q]), acc[mb], 0, 0, 0);
             }
         }
-    };
-    // Whole passes of U steps (a shorter last pass would cost one round trip per step); steps past
-    // the slice load clamped addresses (cache hits) and are zeroed by the activation mask.
-    constexpr int U = MB == 1 ? kMfmaSteps : kMfmaSteps / 2;
-    for (int s0 = 0; s0 < nsteps; s0 += U) pass(std::integral_constant<int, U>(), s0);
+        // single buffer: refill once this pass's reads have been consumed by the products
+        if constexpr (!DB) {
+            if (p + 1 < npass) stage(p + 1, stg);
+        }
+    }
 
     // C tile of this wave: lane holds C[m = 16 mb + 4 kq + e][row rj]; the k-split waves of a unit
     // group are summed from LDS.  Sums of squares: over the 4 k groups of an activation row.  The
     // combine arrays reuse the stage buffers once every wave is past its last pass.
-#if FSVD_RD_MFMA_LDS
     __syncthreads();
     float (*red)[32][kMfmaRows] = reinterpret_cast<float (*)[32][kMfmaRows]>(rd_stage);
     float (*red_ss)[32] = reinterpret_cast<float (*)[32]>(reinterpret_cast<float*>(rd_stage) + kMaxWaves * 32 * kMfmaRows);
-#else
-    __shared__ float red[kMaxWaves][32][kMfmaRows];
-    __shared__ float red_ss[kMaxWaves][32];
-#endif
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -662,23 +661,37 @@ int plan_rows(RowdotArgs& a, int epi, int rows, bool mfma) {
     return blk;
 }
 
-template <int EPI>
-fsvd_status_t launch_mfma(const RowdotArgs& a, int grid, hipStream_t st) {
+template <int MB, int EPI, bool DB>
+fsvd_status_t launch_mfma_t(const RowdotArgs& a, int grid, hipStream_t st) {
     // the stages, or the combine arrays that reuse them, whichever is larger
     constexpr size_t kRed = (size_t)kMaxWaves * 32 * (kMfmaRows + 1) * sizeof(float);
-    const size_t lds1 = FSVD_RD_MFMA_LDS ? std::max((size_t)a.waves * mfma_stage_slots<1>() * 16, kRed) : 0;
-    const size_t lds2 = FSVD_RD_MFMA_LDS ? std::max((size_t)a.waves * mfma_stage_slots<2>() * 16, kRed) : 0;
-    static bool attr_set = false;  // the dynamic LDS limit (up to 64 KiB of stages) raised once
+    constexpr size_t kStage = (size_t)mfma_stage_slots<MB>() * 16 * (DB ? 2 : 1);
+    const size_t lds = std::max((size_t)a.waves * kStage, kRed);
+    static bool attr_set = false;  // the dynamic LDS limit raised once per kernel
     if (!attr_set) {
-        (void)hipFuncSetAttribute((const void*)rowdot_mfma_kernel<1, EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)(kMaxWaves * mfma_stage_slots<1>() * 16));
-        (void)hipFuncSetAttribute((const void*)rowdot_mfma_kernel<2, EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)(kMaxWaves * mfma_stage_slots<2>() * 16));
+        (void)hipFuncSetAttribute((const void*)rowdot_mfma_kernel<MB, EPI, DB>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)std::max(kMaxWaves * kStage, kRed));
         attr_set = true;
     }
-    if (a.M <= 16) rowdot_mfma_kernel<1, EPI><<<grid, 64 * a.waves, lds1, st>>>(a);
-    else rowdot_mfma_kernel<2, EPI><<<grid, 64 * a.waves, lds2, st>>>(a);
+    rowdot_mfma_kernel<MB, EPI, DB><<<grid, 64 * a.waves, lds, st>>>(a);
     return check_launch("rowdot_mfma");
+}
+
+// Waves with 3 or more passes over their slice of the reduction (long K over few factor-row
+// tiles, e.g. the down projection's phase 1) double-buffer their stage, so each pass's factor
+// rows are loaded while the previous pass computes; the doubled stage leaves one 8-wave
+// workgroup per CU, which the launches with 1-2 passes per wave keep for occupancy instead.
+template <int EPI>
+fsvd_status_t launch_mfma(const RowdotArgs& a, int grid, hipStream_t st) {
+    int kmax = 0;
+    for (int i = 0; i < a.nseg; ++i) kmax = std::max(kmax, std::max(a.seg[i].K, EPI == EPI_SWIGLU ? a.seg[i].K2 : 0));
+    const int steps = ((kmax + 31) / 32 + a.ksplit - 1) / a.ksplit;  // 32-wide k steps per wave
+    if (a.M <= 16) {
+        const bool db = (steps + mfma_pass_steps<1>() - 1) / mfma_pass_steps<1>() >= 3;
+        return db ? launch_mfma_t<1, EPI, true>(a, grid, st) : launch_mfma_t<1, EPI, false>(a, grid, st);
+    }
+    const bool db = (steps + mfma_pass_steps<2>() - 1) / mfma_pass_steps<2>() >= 3;
+    return db ? launch_mfma_t<2, EPI, true>(a, grid, st) : launch_mfma_t<2, EPI, false>(a, grid, st);
 }
 
 }  // namespace
