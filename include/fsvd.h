@@ -128,7 +128,9 @@ fsvd_status_t fsvd_prepack_colscale(void* dst, int64_t ld_dst, int64_t cols_pad,
  * x [M, K] (ldx), Ut [r, K] (ldu), Vt [N, r] (ldv), bias [N] or NULL, residual [M, N] (ldr)
  * or NULL (may alias y for in-place accumulation), y [M, N] (ldy).  dtype FSVD_F32 or FSVD_BF16.
  * Decode-sized M (<= 32) runs the HBM-streaming row-dot kernels (z passes through the
- * workspace as a B x r vector); larger M runs the bf16 MFMA path (bf16 only).
+ * workspace as a B x r vector; bf16 launches of 5..32 rows also keep a 1.25 MiB slice there for
+ * the partial tiles of reductions split across workgroups); larger M runs the bf16 MFMA path
+ * (bf16 only).
  * ------------------------------------------------------------------------------------------ */
 size_t fsvd_lowrank_linear_ws(int64_t M, int64_t K, int64_t r, int64_t N, fsvd_dtype_t dtype);
 fsvd_status_t fsvd_lowrank_linear(const void* x, int64_t M, int64_t K, int64_t ldx,

@@ -95,6 +95,7 @@ struct Carve {
 struct LinearBufs {
     void* z;        // [M, r] (dtype)
     int* err;
+    float* part;    // row-dot split-reduction partials (rowdot_part_bytes), or NULL
 };
 
 fsvd_status_t enqueue_linear(const void* x, int M, int K, int64_t ldx, const void* Ut, int r, int64_t ldu,
@@ -106,10 +107,11 @@ fsvd_status_t enqueue_linear(const void* x, int M, int K, int64_t ldx, const voi
         a.nseg = 1;
         a.act = x; a.lda = ldx; a.M = M; a.err = wb.err;
         a.seg[0].W = Ut; a.seg[0].ldw = ldu; a.seg[0].N = r; a.seg[0].K = K; a.seg[0].out = wb.z; a.seg[0].ldo = r;
+        a.part = wb.part;
         TRY(launch_rowdot(a, EPI_Z, dt, st));
         RowdotArgs b{};
         b.nseg = 1;
-        b.act = wb.z; b.lda = r; b.M = M; b.err = wb.err;
+        b.act = wb.z; b.lda = r; b.M = M; b.err = wb.err; b.part = wb.part;
         b.seg[0].W = Vt; b.seg[0].ldw = ldv; b.seg[0].N = N; b.seg[0].K = r; b.seg[0].out = y; b.seg[0].ldo = ldy;
         b.bias = bias; b.residual = residual; b.ldr = ldr;
         b.adv_seqlens = adv; b.adv_B = advB; b.adv_n = advn;
@@ -139,10 +141,11 @@ struct QkvBufs {
     void* xn;      // MFMA path: [M, d] bf16
     float* rstd;   // MFMA path: [M]
     int* err;
+    float* part;   // row-dot split-reduction partials, or NULL
 };
 
 size_t qkv_scratch(int64_t M, int64_t d, int64_t rtot) {
-    size_t s = align256((size_t)M * rtot * 2);
+    size_t s = align256((size_t)M * rtot * 2) + align256(rowdot_part_bytes(M, FSVD_BF16));
     if (M > kRowdotMaxM) s += align256((size_t)M * d * 2) + align256((size_t)M * 4);
     return s;
 }
@@ -159,10 +162,11 @@ fsvd_status_t enqueue_qkv(const QkvDims& q, const void* x, bool norm, const void
         a.act = x; a.lda = q.d; a.M = M; a.err = wb.err;
         a.norm = norm; a.norm_w = (const bf16_t*)norm_w; a.norm_eps = q.eps; a.norm_K = q.d;
         a.seg[0].W = A; a.seg[0].ldw = q.d; a.seg[0].N = rtot; a.seg[0].K = q.d; a.seg[0].out = wb.z; a.seg[0].ldo = rtot;
+        a.part = wb.part;
         TRY(launch_rowdot(a, EPI_Z, FSVD_BF16, st));
         RowdotArgs b{};
         b.nseg = 3;
-        b.act = wb.z; b.lda = rtot; b.M = M; b.err = wb.err;
+        b.act = wb.z; b.lda = rtot; b.M = M; b.err = wb.err; b.part = wb.part;
         b.S = q.S; b.Hq = q.Hq; b.Hkv = q.Hkv; b.D = q.D; b.rope_theta = q.theta; b.L_max = q.L_max;
         b.rope_base = q.theta > 0.f ? std::pow((double)q.theta, -2.0 / (double)q.D) : 0.0;
         b.seqlens = seqlens; b.k_cache = (bf16_t*)kc; b.v_cache = (bf16_t*)vc;
@@ -220,10 +224,12 @@ struct MlpBufs {
     void* xn;     // MFMA path: [M, d]
     float* rstd;  // MFMA path: [M]
     int* err;
+    float* part;  // row-dot split-reduction partials, or NULL
 };
 
 size_t mlp_scratch(int64_t M, int64_t d, int64_t rgu, int64_t d_ff, int64_t rd) {
-    size_t s = align256((size_t)M * rgu * 2) + align256((size_t)M * d_ff * 2) + align256((size_t)M * rd * 2);
+    size_t s = align256((size_t)M * rgu * 2) + align256((size_t)M * d_ff * 2) + align256((size_t)M * rd * 2) +
+               align256(rowdot_part_bytes(M, FSVD_BF16));
     if (M > kRowdotMaxM) s += align256((size_t)M * d * 2) + align256((size_t)M * 4);
     return s;
 }
@@ -238,10 +244,11 @@ fsvd_status_t enqueue_mlp(const MlpDims& p, const void* x, bool norm, const void
         a.act = x; a.lda = p.d; a.M = p.M; a.err = wb.err;
         a.norm = norm; a.norm_w = (const bf16_t*)norm_w; a.norm_eps = p.eps; a.norm_K = p.d;
         a.seg[0].W = A_gu; a.seg[0].ldw = p.d; a.seg[0].N = rgu; a.seg[0].K = p.d; a.seg[0].out = wb.z_gu; a.seg[0].ldo = rgu;
+        a.part = wb.part;
         TRY(launch_rowdot(a, EPI_Z, FSVD_BF16, st));
         RowdotArgs b{};
         b.nseg = 1;
-        b.act = wb.z_gu; b.lda = rgu; b.M = p.M; b.err = wb.err;
+        b.act = wb.z_gu; b.lda = rgu; b.M = p.M; b.err = wb.err; b.part = wb.part;
         if (p.act == FSVD_ACT_SWIGLU) {
             b.seg[0].W = Vg; b.seg[0].ldw = p.rg; b.seg[0].K = p.rg; b.seg[0].act_off = 0;
             b.seg[0].W2 = Vu; b.seg[0].ldw2 = p.ru; b.seg[0].K2 = p.ru; b.seg[0].act_off2 = p.rg;
@@ -252,7 +259,7 @@ fsvd_status_t enqueue_mlp(const MlpDims& p, const void* x, bool norm, const void
             b.seg[0].N = p.d_ff; b.seg[0].out = wb.t; b.seg[0].ldo = p.d_ff;
             TRY(launch_rowdot(b, EPI_GELU, FSVD_BF16, st));
         }
-        LinearBufs lb{wb.z_d, wb.err};
+        LinearBufs lb{wb.z_d, wb.err, wb.part};
         return enqueue_linear(wb.t, p.M, p.d_ff, p.d_ff, Ud, p.rd, p.d_ff, Vd, p.d, p.rd, nullptr, residual, p.d, y,
                               p.d, FSVD_BF16, lb, adv, advB, advn, st);
     }
@@ -279,7 +286,7 @@ fsvd_status_t enqueue_mlp(const MlpDims& p, const void* x, bool norm, const void
         h.Bm = (const bf16_t*)Vu; h.ldb = p.ru; h.K = p.ru; h.a_col_off = p.rg;
         TRY(launch_gemm(h, GEPI_GELU, st));
     }
-    LinearBufs lb{wb.z_d, wb.err};
+    LinearBufs lb{wb.z_d, wb.err, nullptr};
     return enqueue_linear(wb.t, p.M, p.d_ff, p.d_ff, Ud, p.rd, p.d_ff, Vd, p.d, p.rd, nullptr, residual, p.d, y, p.d,
                           FSVD_BF16, lb, adv, advB, advn, st);
 }
@@ -314,6 +321,7 @@ struct LayerPlan {
     int nsplit;
     void* z_o;
     MlpBufs mb;
+    float* part;
 };
 
 LayerPlan plan_layer(const fsvd_decoder_layer_desc* d, void* ws) {
@@ -339,6 +347,11 @@ LayerPlan plan_layer(const fsvd_decoder_layer_desc* d, void* ws) {
     if (M > kRowdotMaxM) {
         p.mb.xn = p.qb.xn;   // the qkv normalised input is dead by the time the MLP runs
         p.mb.rstd = p.qb.rstd;
+    }
+    if (rowdot_part_bytes(M, FSVD_BF16)) {  // one partials slice, used by one launch at a time
+        p.part = (float*)c.take(rowdot_part_bytes(M, FSVD_BF16));
+        p.qb.part = p.part;
+        p.mb.part = p.part;
     }
     int* err = ws ? (int*)ws : nullptr;
     p.qb.err = err;
@@ -388,7 +401,7 @@ fsvd_status_t enqueue_layer(const fsvd_decoder_layer_desc* d, hipStream_t st) {
     TRY(enqueue_attn(p.q, d->k_cache, d->v_cache, d->L_max, d->cache_seqlens, B, S, (int)d->Hq, (int)d->Hkv,
                      (int)d->D, d->softmax_scale, 1, p.o, p.attn_part, p.nsplit, p.qb.err, st));
     const int qdim = (int)(d->Hq * d->D);
-    LinearBufs lb{p.z_o, p.qb.err};
+    LinearBufs lb{p.z_o, p.qb.err, p.part};
     TRY(enqueue_linear(p.o, M, qdim, qdim, d->Ut_o, (int)d->r_o, qdim, d->Vt_o, (int)d->d, d->r_o, nullptr, d->x, d->d,
                        p.h, d->d, FSVD_BF16, lb, nullptr, 0, 0, st));
     MlpDims md{M, (int)d->d, (int)d->r_g, (int)d->r_u, (int)d->d_ff, (int)d->r_d, d->norm_eps, FSVD_ACT_SWIGLU};
@@ -480,7 +493,7 @@ extern "C" {
 
 size_t fsvd_lowrank_linear_ws(int64_t M, int64_t K, int64_t r, int64_t N, fsvd_dtype_t dtype) {
     (void)K; (void)N;
-    return kWsHeader + align256((size_t)M * r * esize(dtype));
+    return kWsHeader + align256((size_t)M * r * esize(dtype)) + align256(rowdot_part_bytes(M, dtype));
 }
 
 fsvd_status_t fsvd_lowrank_linear(const void* x, int64_t M, int64_t K, int64_t ldx, const void* Ut, int64_t r,
@@ -498,7 +511,9 @@ fsvd_status_t fsvd_lowrank_linear(const void* x, int64_t M, int64_t K, int64_t l
     const size_t need = fsvd_lowrank_linear_ws(M, K, r, N, dtype);
     if (ws_bytes < need) return fail(FSVD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
     Carve c(ws);
-    LinearBufs lb{c.take((size_t)M * r * esize(dtype)), (int*)ws};
+    void* z = c.take((size_t)M * r * esize(dtype));
+    float* part = rowdot_part_bytes(M, dtype) ? (float*)c.take(rowdot_part_bytes(M, dtype)) : nullptr;
+    LinearBufs lb{z, (int*)ws, part};
     return enqueue_linear(x, (int)M, (int)K, ldx, Ut, (int)r, ldu, Vt, (int)N, ldv, bias, residual, ldr, y, ldy, dtype,
                           lb, nullptr, 0, 0, (hipStream_t)stream);
 }
@@ -537,6 +552,7 @@ fsvd_status_t fsvd_lowrank_qkv(const void* x, int64_t B, int64_t S, int64_t d, c
         qb.xn = c.take((size_t)M * d * 2);
         qb.rstd = (float*)c.take((size_t)M * 4);
     }
+    if (rowdot_part_bytes(M, FSVD_BF16)) qb.part = (float*)c.take(rowdot_part_bytes(M, FSVD_BF16));
     qb.err = (int*)ws;
     QkvDims qd{(int)B, (int)S, (int)d, (int)r_q, (int)r_k, (int)r_v, (int)Hq, (int)Hkv, (int)D, L_max, norm_eps, rope_theta};
     return enqueue_qkv(qd, x, norm_w != nullptr, norm_w, A_qkv, Vt_q, Vt_k, Vt_v, q_out, k_cache, v_cache, cache_seqlens, k_out, v_out, qb,
@@ -578,6 +594,7 @@ fsvd_status_t fsvd_lowrank_mlp_packed(const void* x, int64_t M, int64_t d, const
         mb.xn = c.take((size_t)M * d * 2);
         mb.rstd = (float*)c.take((size_t)M * 4);
     }
+    if (rowdot_part_bytes(M, FSVD_BF16)) mb.part = (float*)c.take(rowdot_part_bytes(M, FSVD_BF16));
     mb.err = (int*)ws;
     MlpDims md{(int)M, (int)d, (int)r_g, (int)r_u, (int)d_ff, (int)r_d, norm_eps, act};
     return enqueue_mlp(md, x, norm_w != nullptr, norm_w, A_gu, Vt_g, Vt_u, Ut_d, Vt_d, residual, y, mb, nullptr, 0, 0, (hipStream_t)stream);

@@ -37,6 +37,11 @@ struct RowdotArgs {
     int nseg;
     int ksplit;      // waves sharing one row group (split of the reduction): 1, 2, 4 or 8
     int waves;       // waves per workgroup: 4 or 8
+    // matrix-core launches with few tiles: the reduction is also split over kpart workgroups
+    // (set by the planner when part is given); partial tiles go to part and a second kernel
+    // sums them and runs the epilogue.  nblk: tiles (workgroups per reduction part).
+    int kpart, nblk;
+    float* part;     // fp32 partial tiles, rowdot_part_bytes(M, dtype) bytes (NULL: no split)
     const void* act; // [M, lda]
     int64_t lda;
     int M;
@@ -67,6 +72,8 @@ struct RowdotArgs {
 fsvd_status_t launch_rowdot(const RowdotArgs& a, int epi, fsvd_dtype_t dtype, hipStream_t st);
 // Helper filling seg.blk_begin / units_per_blk and returning the total grid size.
 int rowdot_plan(RowdotArgs& a, int epi, fsvd_dtype_t dtype);
+// Workspace bytes a row-dot launch of M activation rows may use for split-reduction partials.
+size_t rowdot_part_bytes(int64_t M, fsvd_dtype_t dtype);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {

@@ -40,6 +40,7 @@ constexpr int kMaxWaves = 8; // waves per workgroup (4 or 8, chosen per launch)
 #ifndef FSVD_RD_WAVES
 #define FSVD_RD_WAVES 2048  // the split is doubled while the launch has fewer waves than this
 #endif
+constexpr size_t kRdPartBytes = (size_t)1280 * 1024;  // split-reduction partial tiles per launch
 
 template <typename T>
 struct Vec;
@@ -406,11 +407,28 @@ constexpr int mfma_pass_steps() { return MB == 1 ? kMfmaSteps : kMfmaSteps / 2; 
 template <int MB>
 constexpr int mfma_stage_slots() { return kMfmaRows * mfma_pass_steps<MB>() * 4; }
 
+// Segment of workgroup tile blk (Q/K/V launches hold up to three)
+template <int EPI>
+__device__ __forceinline__ RowdotSeg seg_of(const RowdotArgs& a, int blk) {
+    const int si = EPI != EPI_QKV ? 0
+                   : ((a.nseg > 2 && blk >= a.seg[2].blk_begin) ? 2 : ((a.nseg > 1 && blk >= a.seg[1].blk_begin) ? 1 : 0));
+    return EPI != EPI_QKV ? a.seg[0] : (si == 0 ? a.seg[0] : (si == 1 ? a.seg[1] : a.seg[2]));
+}
+
+// Values one tile of workgroups leaves when its reduction is split over kpart workgroups: the
+// k-split-reduced C values (g, h, r, m) and the RMSNorm sums of squares (g, m).
+__host__ __device__ inline int part_vals(int ngroups, int ns) { return ngroups * ns * kMfmaRows * 32 + ngroups * 32; }
+__host__ __device__ inline int part_val_idx(int g, int h, int r, int m, int ns) { return ((g * ns + h) * kMfmaRows + r) * 32 + m; }
+__host__ __device__ inline int part_ss_idx(int g, int m, int ngroups, int ns) { return ngroups * ns * kMfmaRows * 32 + g * 32 + m; }
+
 template <int MB, int EPI, bool DB>
 __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
     using T = bf16_t;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int bid = blockIdx.x;
+    // workgroup = (tile blk, reduction part kp): with kpart > 1 the reduction of a tile is split
+    // over kpart workgroups whose partial tiles a second kernel sums
+    const int bid = (a.kpart > 1) ? (int)(blockIdx.x % a.nblk) : (int)blockIdx.x;
+    const int kp = (a.kpart > 1) ? (int)(blockIdx.x / a.nblk) : 0;
     const int si = EPI != EPI_QKV ? 0
                    : ((a.nseg > 2 && bid >= a.seg[2].blk_begin) ? 2 : ((a.nseg > 1 && bid >= a.seg[1].blk_begin) ? 1 : 0));
     const RowdotSeg sg = EPI != EPI_QKV ? a.seg[0] : (si == 0 ? a.seg[0] : (si == 1 ? a.seg[1] : a.seg[2]));
@@ -459,8 +477,9 @@ __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
 
     constexpr int SE = 32;  // k per MFMA step
     const int kmax = (EPI == EPI_SWIGLU) ? max(sg.K, sg.K2) : sg.K;
-    const int st_per = ((kmax + SE - 1) / SE + ksplit - 1) / ksplit;
-    const int k_lo = ks * st_per * SE;
+    const int nparts = ksplit * a.kpart;  // slices of the reduction: ksplit waves x kpart workgroups
+    const int st_per = ((kmax + SE - 1) / SE + nparts - 1) / nparts;
+    const int k_lo = (kp * ksplit + ks) * st_per * SE;
     const int k_hi = min(kmax, k_lo + st_per * SE);
     const int kw = EPI == EPI_SWIGLU ? (half ? sg.K2 : sg.K) : sg.K;
     const int k_end = min(k_hi, kw);
@@ -576,9 +595,6 @@ __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
     }
     __syncthreads();
 
-    if constexpr (EPI == EPI_LINEAR) {
-        if (a.adv_seqlens != nullptr && bid == 0 && tid < a.adv_B) a.adv_seqlens[tid] += a.adv_n;
-    }
     auto sum_waves = [&](int w0, auto get) -> float {
         float s = 0.f;
 #pragma unroll
@@ -594,8 +610,58 @@ __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
     auto ssq = [&](int g, int m) -> float {
         return sum_waves(g * NS * ksplit, [&](int w) { return red_ss[w][m]; });
     };
-    rowdot_epilogue<T, EPI>(a, sg, (bid - sg.blk_begin) * sg.units_per_blk, a.waves / (NS * ksplit), upw,
-                            kMfmaRows / 2, n_units, tid, 64 * a.waves, val, ssq);
+    const int ngroups = a.waves / (NS * ksplit);
+    if (a.kpart > 1) {  // partial tile of this reduction part; rowdot_part_reduce finishes it
+        const int nv = part_vals(ngroups, NS);
+        float* dst = a.part + ((int64_t)kp * a.nblk + bid) * nv;
+        for (int idx = tid; idx < nv; idx += 64 * a.waves) {
+            const int nval = ngroups * NS * kMfmaRows * 32;
+            float v;
+            if (idx < nval) {
+                const int m = idx % 32, r = (idx / 32) % kMfmaRows, gh = idx / (32 * kMfmaRows);
+                v = (m < a.M) ? val(gh / NS, gh % NS, r, m) : 0.f;
+            } else {
+                const int m = (idx - nval) % 32, g = (idx - nval) / 32;
+                v = (norm && m < a.M) ? ssq(g, m) : 0.f;
+            }
+            dst[idx] = v;
+        }
+        return;
+    }
+    if constexpr (EPI == EPI_LINEAR) {
+        if (a.adv_seqlens != nullptr && bid == 0 && tid < a.adv_B) a.adv_seqlens[tid] += a.adv_n;
+    }
+    rowdot_epilogue<T, EPI>(a, sg, (bid - sg.blk_begin) * sg.units_per_blk, ngroups, upw, kMfmaRows / 2, n_units, tid,
+                            64 * a.waves, val, ssq);
+}
+
+// Second kernel of a split reduction: workgroup blk sums the kpart partial tiles of tile blk and
+// runs the epilogue of the unsplit kernel on them (same threads, same unit mapping).
+template <int EPI>
+__global__ __launch_bounds__(512) void rowdot_part_reduce(const RowdotArgs a) {
+    using T = bf16_t;
+    const int tid = threadIdx.x, bid = blockIdx.x;
+    const RowdotSeg sg = seg_of<EPI>(a, bid);
+    constexpr int NS = EPI == EPI_SWIGLU ? 2 : 1;
+    const bool paired = seg_paired(EPI, sg.kind);
+    const int upw = paired ? kMfmaRows / 2 : kMfmaRows;
+    const int n_units = (EPI == EPI_QKV && paired) ? sg.N / 2 : sg.N;
+    const int ngroups = a.waves / (NS * a.ksplit);
+    const int nv = part_vals(ngroups, NS);
+    const float* src = a.part + (int64_t)bid * nv;
+    const int64_t pstride = (int64_t)a.nblk * nv;
+    auto sum_parts = [&](int idx) -> float {
+        float s = 0.f;
+        for (int p = 0; p < a.kpart; ++p) s += src[p * pstride + idx];
+        return s;
+    };
+    auto val = [&](int g, int h, int r, int m) -> float { return sum_parts(part_val_idx(g, h, r, m, NS)); };
+    auto ssq = [&](int g, int m) -> float { return sum_parts(part_ss_idx(g, m, ngroups, NS)); };
+    if constexpr (EPI == EPI_LINEAR) {
+        if (a.adv_seqlens != nullptr && bid == 0 && tid < a.adv_B) a.adv_seqlens[tid] += a.adv_n;
+    }
+    rowdot_epilogue<T, EPI>(a, sg, (bid - sg.blk_begin) * sg.units_per_blk, ngroups, upw, kMfmaRows / 2, n_units, tid,
+                            64 * a.waves, val, ssq);
 }
 
 template <typename T, int EPI>
@@ -658,7 +724,21 @@ int plan_rows(RowdotArgs& a, int epi, int rows, bool mfma) {
         s.blk_begin = blk;
         blk += (n_units + s.units_per_blk - 1) / s.units_per_blk;
     }
-    return blk;
+    // Very few tiles (at most 512 waves, a quarter of the CUs' worth of 8-wave workgroups, even at
+    // the deepest in-workgroup split): split the reduction over kpart workgroups too, up to
+    // FSVD_RD_WAVES waves, while each wave keeps at least 128 elements and the partial tiles fit
+    // the workspace slice.  (Measured on MI355X: splitting launches of 100-300 workgroups costs
+    // more in the second kernel than it saves; at 32-64 workgroups it pays.)
+    a.nblk = blk;
+    a.kpart = 1;
+    if (mfma && a.part != nullptr && (int64_t)blk * a.waves <= 512) {
+        const int ngroups = a.waves / (wave_sets(epi) * ksplit);
+        const int64_t tile_bytes = (int64_t)part_vals(ngroups, wave_sets(epi)) * (int64_t)sizeof(float);
+        while ((int64_t)blk * a.kpart * a.waves < FSVD_RD_WAVES && kmax / (ksplit * a.kpart * 2) >= 128 &&
+               (int64_t)blk * a.kpart * 2 * tile_bytes <= (int64_t)kRdPartBytes)
+            a.kpart *= 2;
+    }
+    return blk * a.kpart;
 }
 
 template <int MB, int EPI, bool DB>
@@ -685,16 +765,25 @@ template <int EPI>
 fsvd_status_t launch_mfma(const RowdotArgs& a, int grid, hipStream_t st) {
     int kmax = 0;
     for (int i = 0; i < a.nseg; ++i) kmax = std::max(kmax, std::max(a.seg[i].K, EPI == EPI_SWIGLU ? a.seg[i].K2 : 0));
-    const int steps = ((kmax + 31) / 32 + a.ksplit - 1) / a.ksplit;  // 32-wide k steps per wave
+    const int steps = ((kmax + 31) / 32 + a.ksplit * a.kpart - 1) / (a.ksplit * a.kpart);  // 32-wide k steps per wave
+    fsvd_status_t s;
     if (a.M <= 16) {
         const bool db = (steps + mfma_pass_steps<1>() - 1) / mfma_pass_steps<1>() >= 3;
-        return db ? launch_mfma_t<1, EPI, true>(a, grid, st) : launch_mfma_t<1, EPI, false>(a, grid, st);
+        s = db ? launch_mfma_t<1, EPI, true>(a, grid, st) : launch_mfma_t<1, EPI, false>(a, grid, st);
+    } else {
+        const bool db = (steps + mfma_pass_steps<2>() - 1) / mfma_pass_steps<2>() >= 3;
+        s = db ? launch_mfma_t<2, EPI, true>(a, grid, st) : launch_mfma_t<2, EPI, false>(a, grid, st);
     }
-    const bool db = (steps + mfma_pass_steps<2>() - 1) / mfma_pass_steps<2>() >= 3;
-    return db ? launch_mfma_t<2, EPI, true>(a, grid, st) : launch_mfma_t<2, EPI, false>(a, grid, st);
+    if (s != FSVD_OK || a.kpart <= 1) return s;
+    rowdot_part_reduce<EPI><<<a.nblk, 64 * a.waves, 0, st>>>(a);
+    return check_launch("rowdot_part_reduce");
 }
 
 }  // namespace
+
+size_t rowdot_part_bytes(int64_t M, fsvd_dtype_t dtype) {
+    return (dtype == FSVD_BF16 && M >= FSVD_RD_MFMA_MIN_M && M <= 32) ? kRdPartBytes : 0;
+}
 
 int rowdot_plan(RowdotArgs& a, int epi, fsvd_dtype_t dtype) {
     const bool mfma = use_mfma(a, epi, dtype);

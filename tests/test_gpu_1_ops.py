@@ -172,10 +172,16 @@ SMALL = I.scaled_decoder(I.CFG2, d=256, Hq=4, Hkv=2, D=64, d_ff=384,
                          ranks={"q": 100, "k": 36, "v": 20, "o": 64, "gate": 72, "up": 88, "down": 48})
 SMALL128 = I.scaled_decoder(I.CFG4, d=512, Hq=8, Hkv=2, D=128, d_ff=640,
                             ranks={"q": 200, "k": 64, "v": 32, "o": 96, "gate": 80, "up": 120, "down": 72})
+# few heads and output columns over long ranks: at 5..32 rows the matrix-core launches have so few
+# tiles that the reduction is also split over workgroups (partial tiles + a reduce kernel), for the
+# RoPE / cache-append and SwiGLU epilogues too
+SPLIT = I.scaled_decoder(I.CFG2, d=256, Hq=2, Hkv=1, D=64, d_ff=256,
+                         ranks={"q": 1016, "k": 1000, "v": 984, "o": 64, "gate": 1008, "up": 1016, "down": 48})
 
 
 @pytest.mark.parametrize("cfg,B,S,seqlens", [(SMALL, 2, 1, [5, 0]), (SMALL, 3, 4, [0, 7, 19]),
-                                             (SMALL128, 4, 1, [60, 3, 0, 57]), (SMALL128, 1, 8, [31])])
+                                             (SMALL128, 4, 1, [60, 3, 0, 57]), (SMALL128, 1, 8, [31]),
+                                             (SPLIT, 8, 1, [0, 1, 2, 30, 31, 40, 62, 63]), (SPLIT, 2, 6, [3, 40])])
 def test_qkv_rope_append(cfg, B, S, seqlens):
     L_max = 64
     say("qkv", cfg.name, cfg.d, cfg.Hq, cfg.Hkv, cfg.D, "B", B, "S", S, seqlens)
@@ -227,7 +233,7 @@ def test_qkv_cache_overflow_sets_error_and_skips_write():
 # ----------------------------------------------------------------------------- MLP (a4)
 
 
-@pytest.mark.parametrize("cfg,M", [(SMALL, 1), (SMALL, 5), (SMALL128, 32), (SMALL128, 3)])
+@pytest.mark.parametrize("cfg,M", [(SMALL, 1), (SMALL, 5), (SMALL128, 32), (SMALL128, 3), (SPLIT, 8), (SPLIT, 24)])
 def test_mlp_swiglu(cfg, M):
     say("mlp swiglu", cfg.name, M)
     p = I.make_decoder_layer(cfg, B=M, S=1, seed=M, random_norm_weights=True)
