@@ -64,7 +64,10 @@ def test_prefill_layer_small_rowdot_path(fold):
     assert rel(lay.y_host(), y_ref) <= BF16_TOL
 
 
-@pytest.mark.parametrize("cfg,B,fold", [(SMALL, 2, False), (SMALL_GQA, 4, False), (SMALL_GQA, 4, True)])
+# batch 8 and 12 run the projections on the matrix cores, and phase 1 of the small GQA layer splits
+# its reduction over workgroups (a reduce kernel in the graph)
+@pytest.mark.parametrize("cfg,B,fold", [(SMALL, 2, False), (SMALL_GQA, 4, False), (SMALL_GQA, 4, True),
+                                        (SMALL_GQA, 8, False), (SMALL, 12, True)])
 def test_graph_replay_equals_eager_and_oracle(cfg, B, fold):
     L_max, L0, N = 96, 20, 6
     say("graph replay", cfg.name, B, "folded" if fold else "")
