@@ -491,10 +491,11 @@ fsvd_status_t launch_t(const GemmArgs& g, hipStream_t st) {
     return check_launch("gemm");
 }
 
-// Tile choice: the largest tile whose grid still covers the 256 CUs (256 x 256 only with at least
-// two workgroups per CU), down to 64 x 128 for small M x N, where a big tile would leave most CUs
-// idle.  The Q/K/V epilogue rotates RoPE pairs (c, c + D/2) inside one wave tile, so with D = 128
-// it needs the 128-wide wave tiles of BN = 256.
+// Tile choice: the largest tile whose grid still covers most of the 256 CUs (256 x 256 from 200
+// tiles: one round on 200-256 CUs beats 1.75-3.25 rounds of 128 x 256 tiles, measured on MI355X
+// for N = 1640 and 3280 at M = 8192), down to 64 x 128 for small M x N, where a big tile would leave
+// most CUs idle.  The Q/K/V epilogue rotates RoPE pairs (c, c + D/2) inside one wave tile, so with
+// D = 128 it needs the 128-wide wave tiles of BN = 256.
 template <int EPI>
 fsvd_status_t launch_epi(const GemmArgs& g, hipStream_t st) {
     auto tiles = [&](int bm, int bn) { return ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn); };
@@ -506,7 +507,7 @@ fsvd_status_t launch_epi(const GemmArgs& g, hipStream_t st) {
         if constexpr (EPI == GEPI_SWIGLU) {
             if (tiles(256, 128) >= 256) return launch_t<256, 128, EPI>(g, st);
         } else {
-            if (tiles(256, 256) >= 512) return launch_t<256, 256, EPI>(g, st);
+            if (tiles(256, 256) >= 200) return launch_t<256, 256, EPI>(g, st);
             if (tiles(128, 256) >= 256 || (EPI == GEPI_QKV && g.D > 64)) return launch_t<128, 256, EPI>(g, st);
         }
         if (tiles(128, 128) >= 256) return launch_t<128, 128, EPI>(g, st);
