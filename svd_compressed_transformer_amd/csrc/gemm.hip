@@ -347,9 +347,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
 #pragma unroll
                     for (int q = 0; q < 8; ++q) {
                         const double tr = (double)p * rev[i0 + q];
-                        const float ang = (float)((tr - floor(tr)) * 6.283185307179586476925286766559);
-                        float c, sn;
-                        sincosf(ang, &sn, &c);
+                        const float fr = (float)(tr - floor(tr));  // angle in revolutions, [0, 1)
+                        // v_sin_f32 / v_cos_f32 take revolutions (error <= 1.3e-7 on [0, 1), measured)
+                        const float sn = __builtin_amdgcn_sinf(fr), c = __builtin_amdgcn_cosf(fr);
                         const float a = x1[q], bb = x2[q];
                         x1[q] = a * c - bb * sn;
                         x2[q] = bb * c + a * sn;
