@@ -325,6 +325,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
             rev[tid] = rope ? exp2(-2.0 * (double)tid / (double)g.D * log2((double)g.rope_theta)) *
                                   0.15915494309189533576888376337251  // 1 / (2 pi)
                             : 0.0;
+        // per tile row, once: its token position (RoPE) and its destination row offset (-1: the
+        // position is past the cache, nothing is written), so the passes below need no global
+        // load of cache_seqlens and no division
+        int64_t* rpos = reinterpret_cast<int64_t*>(rev + 64);
+        int64_t* rdst = rpos + BM;
+        for (int r = tid; r < BM; r += kThreads) {
+            const int row = m0 + r;
+            int64_t pp = 0, dr = -1;
+            if (row < g.M) {
+                const int b = row / g.S, s = row - b * g.S;
+                pp = (g.seqlens ? (int64_t)g.seqlens[b] : 0) + s;
+                if (g.seg == 0) dr = (int64_t)row * g.N;
+                else if (pp >= 0 && pp < g.L_max) dr = ((int64_t)b * g.L_max + pp) * g.N;
+                else set_dev_error(g.err, FSVD_DEVERR_KV_OVERFLOW);
+            }
+            rpos[r] = pp;
+            rdst[r] = dr;
+        }
         __syncthreads();
         bf16_t* dst = g.seg == 0 ? g.q_out : (g.seg == 1 ? g.k_cache : g.v_cache);
         bf16_t* dbg = g.seg == 1 ? g.k_out : (g.seg == 2 ? g.v_out : nullptr);
@@ -336,10 +354,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
                 const int r = pass * RP + lane / LPR;
                 const int row = wm + i * 32 + r;
                 if (row >= g.M || wn + c2 >= g.N) continue;
-                const int b = row / g.S, s = row - b * g.S;
-                const int64_t p = (g.seqlens ? (int64_t)g.seqlens[b] : 0) + s;
-                const bool write = g.seg == 0 || (p >= 0 && p < g.L_max);
-                if (!write) set_dev_error(g.err, FSVD_DEVERR_KV_OVERFLOW);
+                const int tr_ = row - m0;  // row within the tile
+                const int64_t p = rpos[tr_];
+                const int64_t drow = rdst[tr_];
+                const bool write = drow >= 0;
                 float x1[8], x2[8];
                 ld8(r, c1, x1);
                 ld8(r, c2, x2);
@@ -356,7 +374,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
                     }
                 }
                 const u32x4 v1 = pack8(x1), v2 = pack8(x2);
-                const int64_t drow = g.seg == 0 ? (int64_t)row * g.N : ((int64_t)b * g.L_max + p) * g.N;
                 if (write) {
                     *reinterpret_cast<u32x4*>(dst + drow + wn + c1) = v1;
                     *reinterpret_cast<u32x4*>(dst + drow + wn + c2) = v2;
