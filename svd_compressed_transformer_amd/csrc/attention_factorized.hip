@@ -438,12 +438,9 @@ fsvd_status_t launch_fact(const FactAttnArgs& a, hipStream_t st) {
     const int64_t grid = n_qt * a.B * a.Hq;
     if (grid <= 0) return FSVD_OK;
     if (grid > 0x7fffffff) return fail(FSVD_ERR_UNSUPPORTED, "attention grid too large");
-    static bool attr_set = false;  // the dynamic LDS limit is raised once per process
-    if (!attr_set) {
-        (void)hipFuncSetAttribute((const void*)attn_factorized_mfma<D, QW>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)C::LDS);
-        attr_set = true;
-    }
+    if (const fsvd_status_t s = allow_dynamic_lds((const void*)attn_factorized_mfma<D, QW>, C::LDS,
+                                                  "attn_factorized_mfma"))
+        return s;
     attn_factorized_mfma<D, QW><<<(unsigned)grid, kFThreads, C::LDS, st>>>(a);
     return check_launch("attn_factorized_mfma");
 }

@@ -7,6 +7,7 @@
 #include <cstring>
 #include <mutex>
 #include <set>
+#include <tuple>
 
 #include "kernels.h"
 
@@ -32,6 +33,22 @@ fsvd_status_t fail(fsvd_status_t s, const char* fmt, ...) {
 fsvd_status_t check_launch(const char* what) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(FSVD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return FSVD_OK;
+}
+
+fsvd_status_t allow_dynamic_lds(const void* fn, size_t bytes, const char* what) {
+    static std::mutex mu;
+    static std::set<std::tuple<const void*, int, size_t>> done;  // (kernel, device, bytes) set
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FSVD_ERR_HIP, "%s: hipGetDevice: %s", what, hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_tuple(fn, dev, bytes);
+    if (done.count(key)) return FSVD_OK;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess)
+        return fail(FSVD_ERR_HIP, "%s: raising dynamic LDS to %zu bytes: %s", what, bytes, hipGetErrorString(e));
+    done.insert(key);
     return FSVD_OK;
 }
 

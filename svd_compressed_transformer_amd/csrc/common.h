@@ -174,6 +174,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // status of the last kernel launch
 fsvd_status_t check_launch(const char* what);
+
+// Raises kernel fn's dynamic LDS limit to at least `bytes` on the current device. The attribute
+// is set once per (kernel, device) and size; safe to call from several host threads.
+fsvd_status_t allow_dynamic_lds(const void* fn, size_t bytes, const char* what);
 }  // namespace fsvd
 
 #define FSVD_REQUIRE(cond, ...)                                  \

@@ -498,12 +498,7 @@ template <int BM, int BN, int EPI>
 fsvd_status_t launch_t(const GemmArgs& g, hipStream_t st) {
     const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
     const size_t lds = Tile<BM, BN>::LDS_BYTES;
-    static bool attr_set = false;
-    if (!attr_set) {
-        (void)hipFuncSetAttribute((const void*)gemm_kernel<BM, BN, EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)lds);
-        attr_set = true;
-    }
+    if (const fsvd_status_t s = allow_dynamic_lds((const void*)gemm_kernel<BM, BN, EPI>, lds, "gemm")) return s;
     gemm_kernel<BM, BN, EPI><<<tiles, kThreads, lds, st>>>(g);
     return check_launch("gemm");
 }

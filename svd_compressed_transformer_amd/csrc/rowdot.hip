@@ -747,12 +747,10 @@ fsvd_status_t launch_mfma_t(const RowdotArgs& a, int grid, hipStream_t st) {
     constexpr size_t kRed = (size_t)kMaxWaves * 32 * (kMfmaRows + 1) * sizeof(float);
     constexpr size_t kStage = (size_t)mfma_stage_slots<MB>() * 16 * (DB ? 2 : 1);
     const size_t lds = std::max((size_t)a.waves * kStage, kRed);
-    static bool attr_set = false;  // the dynamic LDS limit raised once per kernel
-    if (!attr_set) {
-        (void)hipFuncSetAttribute((const void*)rowdot_mfma_kernel<MB, EPI, DB>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)std::max(kMaxWaves * kStage, kRed));
-        attr_set = true;
-    }
+    // one limit per kernel (its largest workgroup), so the attribute is set once per device
+    if (const fsvd_status_t s = allow_dynamic_lds((const void*)rowdot_mfma_kernel<MB, EPI, DB>,
+                                                  std::max(kMaxWaves * kStage, kRed), "rowdot_mfma"))
+        return s;
     rowdot_mfma_kernel<MB, EPI, DB><<<grid, 64 * a.waves, lds, st>>>(a);
     return check_launch("rowdot_mfma");
 }
