@@ -210,14 +210,15 @@ __global__ __launch_bounds__(kFThreads) void attn_factorized_mfma(const FactAttn
     const int nkv = (max(a.rk, a.rv) + kChunk - 1) / kChunk;
     const int ntile = (kend + BKV - 1) / BKV;
 
-    int n_lane[QW], s_lane[QW], n_min[QW];  // keys seen by this lane's query, fewest over the wave
+    int n_lane[QW], s_lane[QW];  // keys seen by this lane's query of each set
+    int n_min_w = a.S;           // fewest keys any query of the wave sees
 #pragma unroll
     for (int qs = 0; qs < QW; ++qs) {
         const int first = q0 + wave * 16 * QW + qs * 16;
         s_lane[qs] = first + li;
         n_lane[qs] = a.causal ? s_lane[qs] + 1 : a.S;
         if (s_lane[qs] >= a.S) n_lane[qs] = 0;
-        n_min[qs] = first + 15 >= a.S ? 0 : (a.causal ? first + 1 : a.S);
+        n_min_w = min(n_min_w, first + 15 >= a.S ? 0 : (a.causal ? first + 1 : a.S));
     }
 
     // rebuild role: waves 0-3 the key tile (transposed), 4-7 the value tile; dimension blocks
@@ -409,9 +410,7 @@ __global__ __launch_bounds__(kFThreads) void attn_factorized_mfma(const FactAttn
                 }
         }
         lds_barrier();
-#pragma unroll
-        for (int qs = 0; qs < QW; ++qs)
-            attn_tile<D>(Ks, Vts, qf[qs], j0, n_lane[qs], n_min[qs], sc, m[qs], l[qs], o[qs], li, lg);
+        attn_tile<D, QW>(Ks, Vts, qf, j0, n_lane, n_min_w, sc, m, l, o, li, lg);
     }
 
 #pragma unroll

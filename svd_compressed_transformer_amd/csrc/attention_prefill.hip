@@ -1,8 +1,10 @@
 // Attention of several new tokens per sequence (prefill, encoder layers) over the contiguous
 // dense KV cache, on the matrix cores (gfx950, v_mfma_f32_16x16x32_bf16).
 //
-// A workgroup owns 64 consecutive queries of one (sequence, query head); each of its 4 waves owns
-// 16 of them.  Key/value tiles of 64 positions are staged in LDS (K row-major, V transposed so
+// A workgroup owns 64 x QW consecutive queries of one (sequence, query head); each of its 4 waves
+// owns QW sets of 16 (set q of wave w: queries q*64 + w*16 .. +15 of the block, so causal work is
+// balanced over the waves) and every K/V fragment it reads from LDS feeds the products of all its
+// sets.  Key/value tiles of 64 positions are staged in LDS (K row-major, V transposed so
 // keys are contiguous) with XOR-swizzled chunk positions, prefetched into registers one tile
 // ahead.  Each wave computes S^T = K . Q^T (keys x queries) so that a lane ends up holding the
 // scores of ONE query for 16 keys; after the online-softmax update those probabilities are
@@ -18,8 +20,9 @@ namespace fsvd {
 
 namespace {
 
-template <int D>
-__global__ __launch_bounds__(256) void attn_prefill_mfma(const AttnArgs a) {
+template <int D, int QW>
+__global__ __launch_bounds__(256, 2) void attn_prefill_mfma(const AttnArgs a) {
+    constexpr int BQW = BQ * QW;      // queries per workgroup
     constexpr int NT = D / 32;        // 32-wide k steps of q . k
     constexpr int ND = D / 16;        // 16-wide d blocks of the output
     constexpr int KCH = D / 8;        // 16-byte chunks per K row
@@ -32,7 +35,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(const AttnArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int n_qt = (a.Sq + BQ - 1) / BQ;
+    const int n_qt = (a.Sq + BQW - 1) / BQW;
     const int bh_count = a.B * a.Hq;
     const int qt = n_qt - 1 - (int)(blockIdx.x / bh_count);
     const int bh = blockIdx.x % bh_count;
@@ -40,29 +43,40 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(const AttnArgs a) {
     const int g = (h * a.Hkv) / a.Hq;
     const int64_t base = a.seqlens[b];
 
-    int64_t kend = a.causal ? base + min(a.Sq, qt * BQ + BQ) : base + a.Sq;
+    int64_t kend = a.causal ? base + min(a.Sq, qt * BQW + BQW) : base + a.Sq;
     if (kend > a.L_max) {
         if (tid == 0 && qt == n_qt - 1) set_dev_error(a.err, FSVD_DEVERR_SEQ_OVERFLOW);
         kend = a.L_max;
     }
-    const int s_lane = qt * BQ + wave * 16 + li;           // this lane's query
-    int64_t n_lane = a.causal ? base + s_lane + 1 : base + a.Sq;
-    if (n_lane > a.L_max) n_lane = a.L_max;
-    if (s_lane >= a.Sq) n_lane = 0;
-    // fewest keys any query of this wave sees (tiles below it need no mask)
-    const int first = qt * BQ + wave * 16;
-    int64_t n_min = a.causal ? base + first + 1 : base + a.Sq;
-    if (n_min > a.L_max) n_min = a.L_max;
-    if (first + 15 >= a.Sq) n_min = 0;
-
-    // Q as the B operand: lane (li, lg) holds q[s_lane][t*32 + lg*8 .. +7]
-    bf16x8_v qf[NT];
+    // per query set: this lane's query, the keys it sees, and the fewest keys any query of the
+    // wave sees (tiles below that need no mask); cache lengths fit int (checked at launch)
+    int s_lane[QW], n_lane[QW];
+    int64_t n_min = a.L_max;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (s_lane < a.Sq) v = *reinterpret_cast<const u32x4*>(a.q + (((int64_t)b * a.Sq + s_lane) * a.Hq + h) * D + t * 32 + lg * 8);
-        qf[t] = __builtin_bit_cast(bf16x8_v, v);
+    for (int q = 0; q < QW; ++q) {
+        const int first = qt * BQW + q * BQ + wave * 16;
+        s_lane[q] = first + li;
+        int64_t nl = a.causal ? base + s_lane[q] + 1 : base + a.Sq;
+        if (nl > a.L_max) nl = a.L_max;
+        if (s_lane[q] >= a.Sq) nl = 0;
+        n_lane[q] = (int)nl;
+        int64_t nm = a.causal ? base + first + 1 : base + a.Sq;
+        if (nm > a.L_max) nm = a.L_max;
+        if (first + 15 >= a.Sq) nm = 0;
+        n_min = min(n_min, nm);
     }
+
+    // Q as the B operand: lane (li, lg) holds q[s_lane[q]][t*32 + lg*8 .. +7]
+    bf16x8_v qf[QW][NT];
+#pragma unroll
+    for (int q = 0; q < QW; ++q)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (s_lane[q] < a.Sq)
+                v = *reinterpret_cast<const u32x4*>(a.q + (((int64_t)b * a.Sq + s_lane[q]) * a.Hq + h) * D + t * 32 + lg * 8);
+            qf[q][t] = __builtin_bit_cast(bf16x8_v, v);
+        }
 
     const int64_t rowstride = (int64_t)a.Hkv * D;
     const bf16_t* kb0 = a.kc + ((int64_t)b * a.L_max * a.Hkv + g) * D;
@@ -113,10 +127,15 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(const AttnArgs a) {
         }
     };
 
-    float m = kNeg, l = 0.f;
-    f32x4 o[ND];
+    float m[QW], l[QW];
+    f32x4 o[QW][ND];
 #pragma unroll
-    for (int i = 0; i < ND; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < QW; ++q) {
+        m[q] = kNeg;
+        l[q] = 0.f;
+#pragma unroll
+        for (int i = 0; i < ND; ++i) o[q][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     const float sc = a.scale * kLog2e;
 
     if (kend > 0) prefetch(0);
@@ -126,35 +145,51 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(const AttnArgs a) {
         __syncthreads();
         if (j0 + BKV < kend) prefetch(j0 + BKV);
 
-        attn_tile<D>(Ks, Vts, qf, (int)j0, (int)n_lane, (int)n_min, sc, m, l, o, li, lg);
+        attn_tile<D, QW>(Ks, Vts, qf, (int)j0, n_lane, (int)n_min, sc, m, l, o, li, lg);
     }
 
-    float lt = l;
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
-    if (s_lane < a.Sq) {
-        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-        bf16_t* orow = a.out + (((int64_t)b * a.Sq + s_lane) * a.Hq + h) * D;
 #pragma unroll
-        for (int db = 0; db < ND; ++db) {
-            const uint2 w = uint2{pack_bf2(o[db][0] * inv, o[db][1] * inv), pack_bf2(o[db][2] * inv, o[db][3] * inv)};
-            *reinterpret_cast<uint2*>(orow + db * 16 + 4 * lg) = w;
+    for (int q = 0; q < QW; ++q) {
+        float lt = l[q];
+        lt += __shfl_xor(lt, 16);
+        lt += __shfl_xor(lt, 32);
+        if (s_lane[q] < a.Sq) {
+            const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+            bf16_t* orow = a.out + (((int64_t)b * a.Sq + s_lane[q]) * a.Hq + h) * D;
+#pragma unroll
+            for (int db = 0; db < ND; ++db) {
+                const uint2 w = uint2{pack_bf2(o[q][db][0] * inv, o[q][db][1] * inv),
+                                      pack_bf2(o[q][db][2] * inv, o[q][db][3] * inv)};
+                *reinterpret_cast<uint2*>(orow + db * 16 + 4 * lg) = w;
+            }
         }
     }
 }
 
+template <int D, int QW>
+fsvd_status_t launch_prefill_t(const AttnArgs& a, hipStream_t st) {
+    const int64_t grid = (int64_t)((a.Sq + BQ * QW - 1) / (BQ * QW)) * a.B * a.Hq;
+    if (grid > 0x7fffffff) return fail(FSVD_ERR_UNSUPPORTED, "attention grid too large");
+    attn_prefill_mfma<D, QW><<<(unsigned)grid, 256, 0, st>>>(a);
+    return check_launch("attn_prefill_mfma");
+}
+
+#ifndef FSVD_PREFILL_QW
+#define FSVD_PREFILL_QW 0  // query sets per wave: 0 = chosen per launch
+#endif
+
 }  // namespace
 
+// Two query sets per wave halve the LDS reads per product but also the workgroup count, so they
+// are used when at least 1024 workgroups of 128 queries remain to fill the 256 CUs.
 fsvd_status_t launch_attn_prefill(const AttnArgs& a, hipStream_t st) {
-    const int n_qt = (a.Sq + BQ - 1) / BQ;
-    const int64_t grid = (int64_t)n_qt * a.B * a.Hq;
-    if (grid <= 0) return FSVD_OK;
-    if (grid > 0x7fffffff) return fail(FSVD_ERR_UNSUPPORTED, "attention grid too large");
+    if (a.Sq <= 0 || a.B <= 0 || a.Hq <= 0) return FSVD_OK;
     if (a.L_max > 0x7fffffff - 64) return fail(FSVD_ERR_UNSUPPORTED, "cache length %lld too large", (long long)a.L_max);
-    if (a.D == 128) attn_prefill_mfma<128><<<(unsigned)grid, 256, 0, st>>>(a);
-    else if (a.D == 64) attn_prefill_mfma<64><<<(unsigned)grid, 256, 0, st>>>(a);
-    else return fail(FSVD_ERR_UNSUPPORTED, "head dim %d not in {64,128}", a.D);
-    return check_launch("attn_prefill_mfma");
+    const int64_t wg2 = (int64_t)((a.Sq + 2 * BQ - 1) / (2 * BQ)) * a.B * a.Hq;
+    const int qw = FSVD_PREFILL_QW ? FSVD_PREFILL_QW : (wg2 >= 1024 ? 2 : 1);
+    if (a.D == 128) return qw == 2 ? launch_prefill_t<128, 2>(a, st) : launch_prefill_t<128, 1>(a, st);
+    if (a.D == 64) return qw == 2 ? launch_prefill_t<64, 2>(a, st) : launch_prefill_t<64, 1>(a, st);
+    return fail(FSVD_ERR_UNSUPPORTED, "head dim %d not in {64,128}", a.D);
 }
 
 }  // namespace fsvd

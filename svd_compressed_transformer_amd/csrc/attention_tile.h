@@ -16,65 +16,77 @@ constexpr int BQ = 64, BKV = 64;  // queries per workgroup (16 per wave), keys p
 
 // One key tile of the MFMA flash attention: the 64 keys j0 .. j0 + 63 staged in LDS (Ks: K rows
 // with XOR-swizzled 16-byte chunks; Vts: V transposed, 4 keys per uint2 per head dimension)
-// against this wave's 16 queries (qf: the B operand, lane (li, lg) holding q[query li][t*32 +
-// lg*8 .. +7]); with MASK, keys at or past n_lane are masked (without it every key of the tile is
-// below every n_lane of the wave).  Updates the running max m, sum l and the O^T accumulators o
-// (lane (li, lg): dims db*16 + 4*lg + 0..3 of query li).  exp2 is the hardware v_exp_f32.
-template <int D, bool MASK>
-__device__ __forceinline__ void attn_tile_m(const u32x4* Ks, const uint2* Vts, const bf16x8_v (&qf)[D / 32], int j0,
-                                            int n_lane, float sc, float& m, float& l, f32x4 (&o)[D / 16], int li,
-                                            int lg) {
+// against QW sets of 16 queries of this wave (qf[q]: the B operand, lane (li, lg) holding
+// q[query li of set q][t*32 + lg*8 .. +7]).  Every K or V fragment read from LDS feeds the
+// matrix-core products of all QW sets, so LDS traffic per product falls as 1 / QW.  With MASK,
+// keys at or past n_lane[q] are masked (without it every key of the tile is below every n_lane of
+// the wave).  Updates the running max m, sum l and the O^T accumulators o (lane (li, lg): dims
+// db*16 + 4*lg + 0..3 of query li).  exp2 is the hardware v_exp_f32.
+template <int D, int QW, bool MASK>
+__device__ __forceinline__ void attn_tile_m(const u32x4* Ks, const uint2* Vts, const bf16x8_v (&qf)[QW][D / 32],
+                                            int j0, const int (&n_lane)[QW], float sc, float (&m)[QW],
+                                            float (&l)[QW], f32x4 (&o)[QW][D / 16], int li, int lg) {
     constexpr int NT = D / 32, ND = D / 16, KCH = D / 8, KSW = KCH - 1;
-    // S^T blocks: lane holds keys j0 + kb*16 + 4*lg + i for query s_lane
-    f32x4 s[4];
+    // S^T blocks: lane holds keys j0 + kb*16 + 4*lg + i for its query of set q
+    f32x4 s[QW][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < QW; ++q) s[q][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int key = kb * 16 + li;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const bf16x8_v kf = __builtin_bit_cast(bf16x8_v, Ks[key * KCH + ((t * 4 + lg) ^ (key & KSW))]);
-            s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[t], s[kb], 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < QW; ++q) s[q][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[q][t], s[q][kb], 0, 0, 0);
         }
     }
-    float tmax = kNeg;
+    bf16x8_v pf[QW][2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int q = 0; q < QW; ++q) {
+        float tmax = kNeg;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float v = s[kb][i] * sc;
-            if constexpr (MASK) v = j0 + kb * 16 + 4 * lg + i < n_lane ? v : kNeg;
-            s[kb][i] = v;
-            tmax = fmaxf(tmax, v);
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v = s[q][kb][i] * sc;
+                if constexpr (MASK) v = j0 + kb * 16 + 4 * lg + i < n_lane[q] ? v : kNeg;
+                s[q][kb][i] = v;
+                tmax = fmaxf(tmax, v);
+            }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float mn = fmaxf(m[q], tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m[q] - mn);
+        float psum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float p = __builtin_amdgcn_exp2f(s[q][kb][i] - mn);
+                if constexpr (MASK) p = s[q][kb][i] > 0.5f * kNeg ? p : 0.f;
+                s[q][kb][i] = p;
+                psum += p;
+            }
+        l[q] = l[q] * alpha + psum;
+        m[q] = mn;
+#pragma unroll
+        for (int i = 0; i < ND; ++i) o[q][i] *= alpha;
+        // P^T of the two 32-key halves as B operands
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            u32x4 pw;
+            pw.x = pack_bf2(s[q][2 * c][0], s[q][2 * c][1]);
+            pw.y = pack_bf2(s[q][2 * c][2], s[q][2 * c][3]);
+            pw.z = pack_bf2(s[q][2 * c + 1][0], s[q][2 * c + 1][1]);
+            pw.w = pack_bf2(s[q][2 * c + 1][2], s[q][2 * c + 1][3]);
+            pf[q][c] = __builtin_bit_cast(bf16x8_v, pw);
         }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float mn = fmaxf(m, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float p = __builtin_amdgcn_exp2f(s[kb][i] - mn);
-            if constexpr (MASK) p = s[kb][i] > 0.5f * kNeg ? p : 0.f;
-            s[kb][i] = p;
-            psum += p;
-        }
-    l = l * alpha + psum;
-    m = mn;
-#pragma unroll
-    for (int i = 0; i < ND; ++i) o[i] *= alpha;
+    }
 
-    // O^T += V^T . P^T over two 32-key halves
+    // O^T += V^T . P^T over the two 32-key halves
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-        u32x4 pw;
-        pw.x = pack_bf2(s[2 * c][0], s[2 * c][1]);
-        pw.y = pack_bf2(s[2 * c][2], s[2 * c][3]);
-        pw.z = pack_bf2(s[2 * c + 1][0], s[2 * c + 1][1]);
-        pw.w = pack_bf2(s[2 * c + 1][2], s[2 * c + 1][3]);
-        const bf16x8_v pf = __builtin_bit_cast(bf16x8_v, pw);
         const int kc0 = 8 * c + lg, kc1 = 8 * c + 4 + lg;
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
@@ -82,19 +94,20 @@ __device__ __forceinline__ void attn_tile_m(const u32x4* Ks, const uint2* Vts, c
             const uint2 lo = Vts[d * 16 + (kc0 ^ (d & 15))];
             const uint2 hi = Vts[d * 16 + (kc1 ^ (d & 15))];
             const bf16x8_v vf = __builtin_bit_cast(bf16x8_v, u32x4{lo.x, lo.y, hi.x, hi.y});
-            o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[db], 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < QW; ++q) o[q][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[q][c], o[q][db], 0, 0, 0);
         }
     }
 }
 
 // The tile step for a wave whose queries all see at least n_min keys: the mask is applied only to
 // tiles that reach n_min.
-template <int D>
-__device__ __forceinline__ void attn_tile(const u32x4* Ks, const uint2* Vts, const bf16x8_v (&qf)[D / 32], int j0,
-                                          int n_lane, int n_min, float sc, float& m, float& l, f32x4 (&o)[D / 16],
-                                          int li, int lg) {
-    if (j0 + BKV <= n_min) attn_tile_m<D, false>(Ks, Vts, qf, j0, n_lane, sc, m, l, o, li, lg);
-    else attn_tile_m<D, true>(Ks, Vts, qf, j0, n_lane, sc, m, l, o, li, lg);
+template <int D, int QW>
+__device__ __forceinline__ void attn_tile(const u32x4* Ks, const uint2* Vts, const bf16x8_v (&qf)[QW][D / 32], int j0,
+                                          const int (&n_lane)[QW], int n_min, float sc, float (&m)[QW], float (&l)[QW],
+                                          f32x4 (&o)[QW][D / 16], int li, int lg) {
+    if (j0 + BKV <= n_min) attn_tile_m<D, QW, false>(Ks, Vts, qf, j0, n_lane, sc, m, l, o, li, lg);
+    else attn_tile_m<D, QW, true>(Ks, Vts, qf, j0, n_lane, sc, m, l, o, li, lg);
 }
 
 }  // namespace

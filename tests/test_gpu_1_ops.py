@@ -327,11 +327,16 @@ def test_attention_decode_poisoned_tail_not_read():
     assert rel(o, O.attention(q, kc0, vc0, sl, causal=True)) <= BF16_TOL
 
 
-@pytest.mark.parametrize("causal", [True, False])
-def test_attention_multi_token(causal):
-    B, Sq, Hq, Hkv, D, L_max = 2, 37, 4, 2, 64, 128
-    sl = [0, 20]
-    say("attn Sq>1", causal)
+# The last two cases have at least 1024 blocks of 128 queries, so the kernel runs two 16-query
+# sets per wave (set q of wave w: queries q*64 + w*16 .. of the block); the first two run one.
+@pytest.mark.parametrize("B,Sq,Hq,Hkv,D,L_max,sl,causal", [
+    (2, 37, 4, 2, 64, 128, [0, 20], True),
+    (2, 37, 4, 2, 64, 128, [0, 20], False),
+    (2, 300, 176, 22, 128, 400, [0, 77], True),         # ragged last block, GQA 8
+    (4, 200, 128, 128, 64, 320, [0, 5, 31, 100], False),
+])
+def test_attention_multi_token(B, Sq, Hq, Hkv, D, L_max, sl, causal):
+    say("attn Sq>1", B, Sq, Hq, Hkv, D, causal)
     q, kc, vc, _ = I.make_attention_case(B, Sq, Hq, Hkv, D, L_max, sl, q_scale=4.0)
     o, ws = _run_attn(q, kc, vc, sl, causal, L_max, Hkv)
     assert rel(o, O.attention(q, kc, vc, sl, causal=causal)) <= BF16_TOL
