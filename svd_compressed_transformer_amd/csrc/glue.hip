@@ -65,22 +65,43 @@ __global__ void seqlens_advance_kernel(int32_t* sl, int64_t B, int32_t n) {
     if (i < B) sl[i] += n;
 }
 
-// rstd[m] = 1/sqrt(mean(x^2) + eps); xn[m, :] = bf16(x * w) (w may be null = ones)
-__global__ __launch_bounds__(256) void rms_prep_kernel(const bf16_t* x, const bf16_t* w, float eps, int64_t d,
-                                                       bf16_t* xn, float* rstd) {
-    const int64_t row = blockIdx.x;
+// rstd[m] = 1/sqrt(mean(x^2) + eps); xn[m, :] = bf16(x * w) (w may be null = ones).  One wave per
+// row, 16-byte loads when d is a multiple of 8 (rows then start 16-byte aligned), else 2-byte
+// loads; the wave's partial sums are reduced with DPP and lane reads.
+__device__ __forceinline__ uint32_t mul_bf2(uint32_t a, uint32_t b) {
+    return pack_bf2(bf_lo(a) * bf_lo(b), bf_hi(a) * bf_hi(b));
+}
+__global__ __launch_bounds__(256) void rms_prep_kernel(const bf16_t* x, const bf16_t* w, float eps, int64_t M,
+                                                       int64_t d, bf16_t* xn, float* rstd) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;  // whole wave
+    const int lane = threadIdx.x & 63;
     const bf16_t* xr = x + row * d;
-    __shared__ float red[4];
     float s = 0.f;
-    for (int64_t i = threadIdx.x; i < d; i += 256) {
-        const float v = bf2f(xr[i]);
-        s += v * v;
-        if (xn) xn[row * d + i] = w ? f2bf(v * bf2f(w[i])) : xr[i];
+    if ((d & 7) == 0) {
+        for (int64_t c = lane; c < d / 8; c += 64) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c * 8);
+            const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s += bf_lo(e[i]) * bf_lo(e[i]) + bf_hi(e[i]) * bf_hi(e[i]);
+            if (xn) {
+                u32x4 o = v;
+                if (w) {
+                    const u32x4 g = *reinterpret_cast<const u32x4*>(w + c * 8);
+                    o = u32x4{mul_bf2(v.x, g.x), mul_bf2(v.y, g.y), mul_bf2(v.z, g.z), mul_bf2(v.w, g.w)};
+                }
+                *reinterpret_cast<u32x4*>(xn + row * d + c * 8) = o;
+            }
+        }
+    } else {
+        for (int64_t i = lane; i < d; i += 64) {
+            const float v = bf2f(xr[i]);
+            s += v * v;
+            if (xn) xn[row * d + i] = w ? f2bf(v * bf2f(w[i])) : xr[i];
+        }
     }
     s = wave_sum(s);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
-    __syncthreads();
-    if (threadIdx.x == 0) rstd[row] = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
+    if (lane == 0) rstd[row] = 1.0f / sqrtf(s / (float)d + eps);
 }
 
 // out[c, r] = in[r, c]: a 64 x 64 tile passes through LDS so both the reads (along rows of in)
@@ -142,7 +163,9 @@ fsvd_status_t launch_transpose(const bf16_t* in, int64_t rows, int64_t cols, int
 fsvd_status_t launch_rms_prep(const bf16_t* x, const bf16_t* w, float eps, int64_t M, int64_t d, bf16_t* xn,
                               float* rstd, hipStream_t st) {
     if (M == 0) return FSVD_OK;
-    rms_prep_kernel<<<(unsigned)M, 256, 0, st>>>(x, w, eps, d, xn, rstd);
+    if ((d & 7) == 0 && (!aligned16(x) || (w && !aligned16(w)) || (xn && !aligned16(xn))))
+        return fail(FSVD_ERR_INVALID_ARG, "rms_prep: x, norm weight and output must be 16-byte aligned");
+    rms_prep_kernel<<<(unsigned)((M + 3) / 4), 256, 0, st>>>(x, w, eps, M, d, xn, rstd);
     return check_launch("rms_prep");
 }
 
