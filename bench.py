@@ -210,16 +210,18 @@ def main():
 
     graphs = [fsvd.fsvd_decoder_layer_capture(d) for d in layers_dec]
 
-    def step():
+    def step(mid=None):
         sl_all.zero_()
         for pre in layers_pre:
             fsvd.fsvd_decoder_layer_run(pre.desc, stream)
+        if mid is not None:
+            mid.record(stream)  # end of the prefill half
         ys_dec[NL - 1].copy_(xs_pre[NL % 2][:, S - 1:S, :])
         for _ in range(ND):
             for g in graphs:
                 fsvd.fsvd_graph_replay(g, stream)
 
-    # split timing of the two phases (same kernels, measured in the warmup)
+    # warmup (the first pass pays first-touch and first-launch costs), with the two halves logged
     e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     for w in range(max(1, args.warmup)):
         sl_all.zero_()
@@ -234,8 +236,6 @@ def main():
         e[2].record(stream)
         torch.cuda.synchronize()
         log(f"warmup {w}: prefill {e[0].elapsed_time(e[1]):.2f} ms, decode {e[1].elapsed_time(e[2]):.2f} ms")
-    t_pre_ms = e[0].elapsed_time(e[1])
-    t_dec_ms = e[1].elapsed_time(e[2])
 
     # a plain device copy of known size (256 MiB read, 256 MiB written): the calibration point of
     # the HBM byte counters in a counter-collection run of this script
@@ -249,15 +249,18 @@ def main():
     assert fsvd.fsvd_poll_device_error(pre_ws, stream) == 0
 
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
+    # timed steps; an event at the end of each step's prefill half splits the step into its prefill
+    # and decode halves (reported below as the means over the timed steps)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
+    ev[0].record(stream)
     for k in range(args.steps):
-        step()
-    t1.record(stream)
+        step(mid=ev[2 * k + 1])
+        ev[2 * k + 2].record(stream)
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
-    log(f"timed: {args.steps} steps, {ms:.2f} ms/step")
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    t_pre_ms = sum(ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(args.steps)) / args.steps
+    t_dec_ms = sum(ev[2 * k + 1].elapsed_time(ev[2 * k + 2]) for k in range(args.steps)) / args.steps
+    log(f"timed: {args.steps} steps, {ms:.2f} ms/step (prefill {t_pre_ms:.2f} ms, decode {t_dec_ms:.2f} ms)")
 
     # ------------------------------------------------ dominant kernel: decode attention, timed live
     # The decode-attention kernel (the largest single consumer of bytes in the step) timed with
