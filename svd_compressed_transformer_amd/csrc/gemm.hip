@@ -37,6 +37,9 @@ constexpr int kThreads = 256;   // 4 waves, arranged 2 x 2
 // BK = 64 slices, one whole 128-byte line per row (the load path serves whole lines about 1.4x
 // faster than half lines), three deep (3 x 48 KiB for 128 x 256).  Measured on MI355X, the deeper
 // pipeline matters more for the big tile.
+#ifndef FSVD_GEMM_SPLITB
+#define FSVD_GEMM_SPLITB 1  // 256 x 256 tiles: B loads of a tile in its second k step
+#endif
 template <int BM, int BN>
 constexpr int kb_for() { return BM + BN > 384 ? 32 : 64; }
 template <int BM, int BN>
@@ -157,7 +160,10 @@ struct Tile {
                                          bf16x8_v (&af)[2][FI], bf16x8_v (&bf)[2][FJ]) {
         const int lane = tid & 63, wave = tid >> 6;
         constexpr int LA = BM * CPR / kThreads, LB = BN * CPR / kThreads;  // loads per operand
-        constexpr int KB_B = KSUB > 2 ? 1 : 0;                             // k step issuing the B loads
+        // k step issuing the B loads; with two k steps per tile (KSUB = 2) they go into the last
+        // one, after the barrier, so each k step carries half of the tile's loads
+        constexpr bool B_LAST = KSUB == 2 && FSVD_GEMM_SPLITB;
+        constexpr int KB_B = KSUB > 2 ? 1 : 0;
         const u32x4* st = smem + (kt % S) * STAGE;
         u32x4* dst = smem + ((kt + S - 1) % S) * STAGE;
 #pragma unroll
@@ -166,10 +172,10 @@ struct Tile {
             read_frags(st, kk + 1, wm, wn, lane, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
             if constexpr (ISSUE) {
                 if (kk == 0) issue_tile<BM, KB>(A, lda, m0, M, (kt + S - 1) * KB, K, dst, wave, lane);
-                if (kk == KB_B) issue_tile<BN, KB>(B, ldb, n0, N, (kt + S - 1) * KB, K, dst + BM * CPR, wave, lane);
+                if (!B_LAST && kk == KB_B) issue_tile<BN, KB>(B, ldb, n0, N, (kt + S - 1) * KB, K, dst + BM * CPR, wave, lane);
             }
             mfmas(af[kk & 1], bf[kk & 1]);
-            constexpr int ng0 = ISSUE ? (KB_B == 0 ? LA + LB : LA) : 0;
+            constexpr int ng0 = ISSUE ? ((KB_B == 0 && !B_LAST) ? LA + LB : LA) : 0;
             constexpr int ng1 = ISSUE ? LB : 0;
             if (kk == 0) sched_interleave<FI + FJ, ng0, FI * FJ>();
             else if (kk == KB_B) sched_interleave<FI + FJ, ng1, FI * FJ>();
@@ -177,8 +183,12 @@ struct Tile {
         }
         __builtin_amdgcn_sched_barrier(0);
         if (kt + 1 < nk) {
-            // tiles issued so far: 0 .. min(kt + S - 1, nk - 1); tile kt + 1 must have landed
-            wait_vm((min(kt + S - 1, nk - 1) - (kt + 1)) * LOADS);
+            // tile kt + 1 must have landed; issued after it so far: the whole tiles up to
+            // min(kt + S - 1, nk - 1), or with B_LAST up to kt + S - 2 plus the A part of kt + S - 1
+            if constexpr (B_LAST)
+                wait_vm(max(0, min(kt + S - 2, nk - 1) - (kt + 1)) * LOADS + (ISSUE ? LA : 0));
+            else
+                wait_vm((min(kt + S - 1, nk - 1) - (kt + 1)) * LOADS);
             if (kt + 1 == nk - 1 && K % KB) {
                 lds_barrier();
                 u32x4* last = smem + ((kt + 1) % S) * STAGE;
@@ -189,8 +199,9 @@ struct Tile {
             __builtin_amdgcn_sched_barrier(0);
             read_frags(smem + ((kt + 1) % S) * STAGE, 0, wm, wn, lane, af[0], bf[0]);
         }
+        if constexpr (ISSUE && B_LAST) issue_tile<BN, KB>(B, ldb, n0, N, (kt + S - 1) * KB, K, dst + BM * CPR, wave, lane);
         mfmas(af[(KSUB - 1) & 1], bf[(KSUB - 1) & 1]);
-        sched_interleave<FI + FJ, 0, FI * FJ>();
+        sched_interleave<FI + FJ, (ISSUE && B_LAST) ? LB : 0, FI * FJ>();
         __builtin_amdgcn_sched_barrier(0);
     }
 
