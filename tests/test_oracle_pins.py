@@ -322,6 +322,74 @@ def pin_prefill_then_decode(O):
     assert rel(kc, kc_all) <= 1e-10 and rel(vc, vc_all) <= 1e-10
 
 
+def _decoder_token_loops(x_row, p, cfg, pos, K_hist, V_hist):
+    """One token of the pre-norm decoder layer written out with the pure-Python loops: RMSNorm,
+    the three low-rank projections, RoPE at ``pos`` on q and k, the new k/v appended to the
+    per-kv-head history lists K_hist[g], V_hist[g] (mutated), softmax attention over the whole
+    history, then h = x + O(o) and y = h + down(SiLU(gate(n)) * up(n)) with n = RMSNorm(h).
+    FlashSVD v1.5 explainer, Methodology 2 (current-token Q/K/V, dense history) and 3 (MLP)."""
+    D, Hq, Hkv = cfg.D, cfg.Hq, cfg.Hkv
+    a = L.rmsnorm_row(x_row, p["attn_norm_w"], cfg.norm_eps)
+    q = L.lowrank_linear([a], p["Ut_q"], p["Vt_q"])[0]
+    k = L.lowrank_linear([a], p["Ut_k"], p["Vt_k"])[0]
+    v = L.lowrank_linear([a], p["Ut_v"], p["Vt_v"])[0]
+    for g in range(Hkv):
+        K_hist[g].append(L.rope_vec(k[g * D:(g + 1) * D], pos, cfg.rope_theta))
+        V_hist[g].append(list(v[g * D:(g + 1) * D]))
+    o = []
+    for h in range(Hq):
+        g = h * Hkv // Hq
+        qh = L.rope_vec(q[h * D:(h + 1) * D], pos, cfg.rope_theta)
+        o += L.softmax_attention_one(qh, K_hist[g], V_hist[g], 1.0 / math.sqrt(D))
+    hrow = L.lowrank_linear([o], p["Ut_o"], p["Vt_o"], residual=[list(map(float, x_row))])[0]
+    n = L.rmsnorm_row(hrow, p["mlp_norm_w"], cfg.norm_eps)
+    gt = L.lowrank_linear([n], p["Ut_gate"], p["Vt_gate"])[0]
+    up = L.lowrank_linear([n], p["Ut_up"], p["Vt_up"])[0]
+    t = [gi / (1.0 + math.exp(-gi)) * ui for gi, ui in zip(gt, up)]
+    return L.lowrank_linear([t], p["Ut_down"], p["Vt_down"], residual=[hrow])[0]
+
+
+def pin_decoder_layer(O):
+    """The decoder-layer composition written out token by token with the loops: one decode step
+    over a cached history, a small causal prefill that starts mid-cache, and two successive decode
+    steps of ``decoder_steps``; outputs and the appended cache rows at 1e-10."""
+    cfg = _small_decoder()
+    rng = np.random.default_rng(31)
+    B, Lmax = 2, 12
+    p = I.make_decoder_layer(cfg, B=B, S=4, seed=17, dtype="bf16", random_norm_weights=True)
+    kc0 = I.round_bf16(rng.standard_normal((B, Lmax, cfg.Hkv, cfg.D)))
+    vc0 = I.round_bf16(rng.standard_normal((B, Lmax, cfg.Hkv, cfg.D)))
+
+    def run_loops(x, sl):
+        Bx, S, _ = np.asarray(x).shape
+        y = np.zeros((Bx, S, cfg.d))
+        kc, vc = np.array(kc0, dtype=float), np.array(vc0, dtype=float)
+        for b in range(Bx):
+            K = [[list(kc0[b, j, g]) for j in range(int(sl[b]))] for g in range(cfg.Hkv)]
+            V = [[list(vc0[b, j, g]) for j in range(int(sl[b]))] for g in range(cfg.Hkv)]
+            for s in range(S):
+                pos = int(sl[b]) + s
+                y[b, s] = _decoder_token_loops(x[b, s], p, cfg, pos, K, V)
+                for g in range(cfg.Hkv):
+                    kc[b, pos, g], vc[b, pos, g] = K[g][-1], V[g][-1]
+        return y, kc, vc
+
+    for S, sl in ((1, np.array([3, 7])), (4, np.array([0, 5]))):
+        x = p["x"][:, :S]
+        y, kc, vc = O.decoder_layer(x, p, cfg, kc0, vc0, sl)
+        y_l, kc_l, vc_l = run_loops(x, sl)
+        assert rel(y, y_l) <= 1e-10, S
+        assert rel(kc, kc_l) <= 1e-10 and rel(vc, vc_l) <= 1e-10
+    # two decode steps: the second reads the first one's appended row
+    sl = np.array([2, 6])
+    xs = np.transpose(p["x"][:, :2], (1, 0, 2))
+    ys, kc, vc, sl2 = O.decoder_steps(xs, p, cfg, kc0, vc0, sl)
+    y_l, kc_l, vc_l = run_loops(p["x"][:, :2], sl)
+    assert list(sl2) == list(sl + 2)
+    assert rel(np.transpose(ys, (1, 0, 2)), y_l) <= 1e-10
+    assert rel(kc, kc_l) <= 1e-10 and rel(vc, vc_l) <= 1e-10
+
+
 def pin_encoder_layer(O):
     cfg = I.EncoderLayerConfig(name="tiny-bert", d=16, H=2, D=8, d_ff=24,
                                ranks={"q": 8, "k": 8, "v": 8, "o": 8, "up": 8, "down": 8})
@@ -413,8 +481,8 @@ def pin_swift_reuse(O):
 PINS = [pin_lowrank_bruteforce, pin_lowrank_golden, pin_lowrank_fullrank_svd, pin_lowrank_eckart_young,
         pin_zero_padding, pin_rmsnorm, pin_layernorm, pin_rope, pin_activations, pin_attention_matrix,
         pin_attention_special, pin_attention_split_merge, pin_attention_gqa, pin_qkv_append_and_packing,
-        pin_lowrank_history_rebuild, pin_mlp_packed, pin_prefill_then_decode, pin_encoder_layer, pin_swift_golden, pin_swift_closed_form,
-        pin_swift_reuse]
+        pin_lowrank_history_rebuild, pin_mlp_packed, pin_prefill_then_decode, pin_decoder_layer, pin_encoder_layer,
+        pin_swift_golden, pin_swift_closed_form, pin_swift_reuse]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -512,7 +580,30 @@ def _mut_swift_ascending(X_batches, W, k):
             "Wk": W @ Vk @ Vk.T, "U": W @ Vk, "V": Vk.T}
 
 
+def _mut_layer(kind):
+    """decoder_layer with one planted slip in its composition."""
+    def layer(x, p, cfg, k_cache, v_cache, cache_seqlens, causal=True):
+        x = np.asarray(x, dtype=float)
+        B, S, d = x.shape
+        q, _, _, kc, vc = O.qkv(x, p["attn_norm_w"], cfg.norm_eps, p["Ut_q"], p["Vt_q"], p["Ut_k"], p["Vt_k"],
+                                p["Ut_v"], p["Vt_v"], cfg.Hq, cfg.Hkv, cfg.D, cfg.rope_theta, k_cache, v_cache,
+                                cache_seqlens)
+        o = O.attention(q, kc, vc, cache_seqlens, causal=causal)
+        h = O.lowrank_linear(o.reshape(B, S, cfg.Hq * cfg.D), p["Ut_o"], p["Vt_o"],
+                             residual=None if kind == "drop_o_residual" else x)
+        mlp_in = x if kind == "mlp_norm_x" else h
+        res = x if kind == "mlp_residual_x" else h
+        y = O.mlp(mlp_in, p["mlp_norm_w"], cfg.norm_eps, "swiglu", p["Ut_gate"], p["Vt_gate"], p["Ut_up"],
+                  p["Vt_up"], p["Ut_down"], p["Vt_down"], residual=res)
+        return y, kc, vc
+    layer.__name__ = f"_mut_layer_{kind}"
+    return layer
+
+
 MUTANTS = [
+    ("decoder_layer", _mut_layer("mlp_residual_x"), pin_decoder_layer),
+    ("decoder_layer", _mut_layer("mlp_norm_x"), pin_decoder_layer),
+    ("decoder_layer", _mut_layer("drop_o_residual"), pin_decoder_layer),
     ("lowrank_linear", _mut_lowrank_transposed, pin_lowrank_bruteforce),
     ("lowrank_linear", _mut_lowrank_drop_bias, pin_lowrank_golden),
     ("rope", _mut_rope_sign, pin_rope),
