@@ -82,6 +82,14 @@ fsvd_status_t need_ld(int64_t ld, int64_t extent, fsvd_dtype_t t, const char* na
     if ((ld * (int64_t)esize(t)) % 16) return fail(FSVD_ERR_INVALID_ARG, "%s * element size must be a multiple of 16 bytes", name);
     return FSVD_OK;
 }
+// a rank above min(K, N) is never the truncation of a K x N map (and a padded rank stays within
+// the bound, K and N being multiples of the padding)
+fsvd_status_t need_rank(int64_t r, int64_t K, int64_t N, const char* name) {
+    if (r > K || r > N)
+        return fail(FSVD_ERR_INVALID_ARG, "%s = %lld exceeds min(K, N) = min(%lld, %lld)", name, (long long)r,
+                    (long long)K, (long long)N);
+    return FSVD_OK;
+}
 fsvd_status_t need_dtype(fsvd_dtype_t t, bool allow_f32) {
     if (t == FSVD_BF16) return FSVD_OK;
     if (t == FSVD_F32 && allow_f32) return FSVD_OK;
@@ -391,6 +399,11 @@ fsvd_status_t validate_layer(const fsvd_decoder_layer_desc* d) {
         TRY(need_vec(ranks[i], t, rn[i]));
     }
     TRY(need_vec(d->d, t, "d")); TRY(need_vec(d->d_ff, t, "d_ff"));
+    const int64_t qd = d->Hq * d->D, kd = d->Hkv * d->D;
+    TRY(need_rank(d->r_q, d->d, qd, "r_q")); TRY(need_rank(d->r_k, d->d, kd, "r_k"));
+    TRY(need_rank(d->r_v, d->d, kd, "r_v")); TRY(need_rank(d->r_o, qd, d->d, "r_o"));
+    TRY(need_rank(d->r_g, d->d, d->d_ff, "r_g")); TRY(need_rank(d->r_u, d->d, d->d_ff, "r_u"));
+    TRY(need_rank(d->r_d, d->d_ff, d->d, "r_d"));
     const void* ptrs[] = {d->x, d->y, d->A_qkv, d->Vt_q, d->Vt_k, d->Vt_v, d->Ut_o, d->Vt_o, d->A_gu, d->Vt_g, d->Vt_u,
                           d->Ut_d, d->Vt_d, d->k_cache, d->v_cache, d->ws};
     const char* pn[] = {"x", "y", "A_qkv", "Vt_q", "Vt_k", "Vt_v", "Ut_o", "Vt_o", "A_gu", "Vt_g", "Vt_u",
@@ -520,6 +533,7 @@ fsvd_status_t fsvd_lowrank_linear(const void* x, int64_t M, int64_t K, int64_t l
     TRY(need_dtype(dtype, true));
     TRY(need_dim(M, "M")); TRY(need_dim(K, "K")); TRY(need_dim(r, "r")); TRY(need_dim(N, "N"));
     TRY(need_vec(K, dtype, "K")); TRY(need_vec(r, dtype, "r")); TRY(need_vec(N, dtype, "N"));
+    TRY(need_rank(r, K, N, "r"));
     TRY(need_ptr(x, "x")); TRY(need_ptr(Ut, "Ut")); TRY(need_ptr(Vt, "Vt")); TRY(need_ptr(y, "y")); TRY(need_ptr(ws, "ws"));
     TRY(opt_ptr(bias, "bias")); TRY(opt_ptr(residual, "residual"));
     TRY(need_ld(ldx, K, dtype, "ldx")); TRY(need_ld(ldu, K, dtype, "ldu")); TRY(need_ld(ldv, r, dtype, "ldv"));
@@ -553,8 +567,9 @@ fsvd_status_t fsvd_lowrank_qkv(const void* x, int64_t B, int64_t S, int64_t d, c
     TRY(need_dim(r_q, "r_q")); TRY(need_dim(r_k, "r_k")); TRY(need_dim(r_v, "r_v"));
     TRY(need_vec(d, dtype, "d")); TRY(need_vec(r_q, dtype, "r_q")); TRY(need_vec(r_k, dtype, "r_k"));
     TRY(need_vec(r_v, dtype, "r_v"));
-    if (D % 2) return fail(FSVD_ERR_INVALID_ARG, "D must be even");
+    if (D != 64 && D != 128) return fail(FSVD_ERR_UNSUPPORTED, "head dim %lld not in {64,128}", (long long)D);
     if (Hq % Hkv) return fail(FSVD_ERR_INVALID_ARG, "Hq must be a multiple of Hkv");
+    TRY(need_rank(r_q, d, Hq * D, "r_q")); TRY(need_rank(r_k, d, Hkv * D, "r_k")); TRY(need_rank(r_v, d, Hkv * D, "r_v"));
     TRY(need_ptr(x, "x")); TRY(need_ptr(A_qkv, "A_qkv")); TRY(need_ptr(Vt_q, "Vt_q")); TRY(need_ptr(Vt_k, "Vt_k"));
     TRY(need_ptr(Vt_v, "Vt_v")); TRY(need_ptr(q_out, "q_out")); TRY(need_ptr(k_cache, "k_cache"));
     TRY(need_ptr(v_cache, "v_cache")); TRY(need_ptr(ws, "ws")); TRY(opt_ptr(norm_w, "norm_w"));
@@ -597,6 +612,7 @@ fsvd_status_t fsvd_lowrank_mlp_packed(const void* x, int64_t M, int64_t d, const
     }
     TRY(need_vec(d, dtype, "d")); TRY(need_vec(d_ff, dtype, "d_ff")); TRY(need_vec(r_g, dtype, "r_g"));
     TRY(need_vec(r_u, dtype, "r_u")); TRY(need_vec(r_d, dtype, "r_d"));
+    TRY(need_rank(r_g, d, d_ff, "r_g")); TRY(need_rank(r_u, d, d_ff, "r_u")); TRY(need_rank(r_d, d_ff, d, "r_d"));
     TRY(need_ptr(x, "x")); TRY(need_ptr(A_gu, "A_gu")); TRY(need_ptr(Vt_u, "Vt_u")); TRY(need_ptr(Ut_d, "Ut_d"));
     TRY(need_ptr(Vt_d, "Vt_d")); TRY(need_ptr(y, "y")); TRY(need_ptr(ws, "ws"));
     TRY(opt_ptr(norm_w, "norm_w")); TRY(opt_ptr(residual, "residual"));

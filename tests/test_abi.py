@@ -120,6 +120,44 @@ def test_validation_errors_return_before_launch(L, monkeypatch):
     assert s == fsvd.FSVD_ERR_INVALID_ARG
 
 
+def test_rank_and_head_dim_bounds(L, monkeypatch):
+    """A rank above min(K, N) and a Q/K/V head dim outside {64, 128} are refused on the host,
+    before anything is enqueued (every pointer below is a fake, never dereferenced)."""
+    monkeypatch.setattr(fsvd, "_s", lambda stream: 0)
+    bf = fsvd.FSVD_BF16
+    P = 0x1000
+    # linear: r = 24 > N = 16, and r = 24 > K = 16
+    s, msg = _status(lambda: fsvd.fsvd_lowrank_linear(P, 1, 64, 64, P, 24, 64, P, 16, 24, None, None, 16, P, 16,
+                                                      bf, P, 1 << 20))
+    assert s == fsvd.FSVD_ERR_INVALID_ARG and "min(K, N)" in msg
+    s, msg = _status(lambda: fsvd.fsvd_lowrank_linear(P, 1, 16, 16, P, 24, 16, P, 64, 24, None, None, 64, P, 64,
+                                                      bf, P, 1 << 20))
+    assert s == fsvd.FSVD_ERR_INVALID_ARG and "min(K, N)" in msg
+    # r == min(K, N) is allowed: fails later only on the workspace size
+    s, _ = _status(lambda: fsvd.fsvd_lowrank_linear(P, 1, 16, 16, P, 16, 16, P, 64, 16, None, None, 64, P, 64,
+                                                    bf, P, 16))
+    assert s == fsvd.FSVD_ERR_WORKSPACE
+    # qkv: head dim 256 (RoPE pairs are handled for D in {64, 128} only), and r_k > Hkv * D
+    s, msg = _status(lambda: fsvd.fsvd_lowrank_qkv(P, 1, 1, 512, None, 0.0, P, 8, 8, 8, P, P, P, 2, 2, 256, 1e4,
+                                                   P, P, P, 8, P, None, None, bf, P, 1 << 20))
+    assert s == fsvd.FSVD_ERR_UNSUPPORTED and "head dim" in msg
+    s, msg = _status(lambda: fsvd.fsvd_lowrank_qkv(P, 1, 1, 512, None, 0.0, P, 64, 136, 8, P, P, P, 2, 2, 64, 1e4,
+                                                   P, P, P, 8, P, None, None, bf, P, 1 << 20))
+    assert s == fsvd.FSVD_ERR_INVALID_ARG and "r_k" in msg
+    # mlp: r_d > min(d_ff, d)
+    s, msg = _status(lambda: fsvd.fsvd_lowrank_mlp_packed(P, 1, 64, None, 0.0, fsvd.FSVD_ACT_SWIGLU, P, 8, 8, P, P,
+                                                          128, P, P, 72, None, P, bf, P, 1 << 20))
+    assert s == fsvd.FSVD_ERR_INVALID_ARG and "r_d" in msg
+    # decoder layer: r_o > d
+    d = fsvd.decoder_layer_desc(B=1, S=1, d=64, Hq=2, Hkv=2, D=64, d_ff=64, L_max=8, r_q=8, r_k=8, r_v=8, r_o=72,
+                                r_g=8, r_u=8, r_d=8, **{k: P * (i + 1) for i, k in enumerate((
+                                    "x", "y", "A_qkv", "Vt_q", "Vt_k", "Vt_v", "Ut_o", "Vt_o", "A_gu", "Vt_g",
+                                    "Vt_u", "Ut_d", "Vt_d", "k_cache", "v_cache", "cache_seqlens", "ws"))})
+    d.ws_bytes = 1 << 30
+    s, msg = _status(lambda: fsvd.fsvd_decoder_layer_run(d))
+    assert s == fsvd.FSVD_ERR_INVALID_ARG and "r_o" in msg
+
+
 def test_binding_refuses_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fsvd, "_lib", None)
     monkeypatch.setattr(fsvd, "LIB_PATH", str(tmp_path / "nope.so"))

@@ -106,20 +106,23 @@ def test_graph_replay_equals_eager_and_oracle(cfg, B, fold):
         fsvd.fsvd_graph_replay(g)
 
 
-def test_stack_graph_equals_per_layer_graphs():
+def test_stack_graph_equals_per_layer_graphs_and_oracle_chain():
     """Three layers chained (y of layer l is x of layer l+1): one whole-stack graph replay per step
-    gives the same bits as three per-layer graph replays, step after step."""
+    gives the same bits as three per-layer graph replays, step after step, and both follow the
+    oracle applied layer after layer (the oracle's own chain: layer l+1 takes the oracle's output of
+    layer l, never the GPU's) over every step, with every layer's cache compared at the end."""
     cfg, B, L_max, L0, N, NL = SMALL_GQA, 3, 64, 10, 4, 3
-    say("stack graph vs per-layer graphs", NL, "layers")
+    say("stack graph vs per-layer graphs vs oracle chain", NL, "layers")
     rng = np.random.default_rng(7)
     xs = I.round_bf16(rng.standard_normal((N, B, cfg.d)))
+    params = [I.make_decoder_layer(cfg, B=B, S=1, seed=40 + l, random_norm_weights=True) for l in range(NL)]
+    hist = [I.make_kv_history(B, L_max, cfg.Hkv, cfg.D, L0, seed=50 + l) for l in range(NL)]
 
     def build():
         lays = []
         for l in range(NL):
-            p = I.make_decoder_layer(cfg, B=B, S=1, seed=40 + l, random_norm_weights=True)
-            kc, vc = I.make_kv_history(B, L_max, cfg.Hkv, cfg.D, L0, seed=50 + l)
-            lays.append(DeviceLayer(cfg, p, B=B, S=1, L_max=L_max, kc=kc, vc=vc, seqlens=np.full(B, L0),
+            kc, vc = hist[l]
+            lays.append(DeviceLayer(cfg, params[l], B=B, S=1, L_max=L_max, kc=kc, vc=vc, seqlens=np.full(B, L0),
                                     advance=True, fold_norm=True))
         for l in range(1, NL):  # chain: layer l reads layer l-1's output
             lays[l].desc.x = lays[l - 1].y.data_ptr()
@@ -128,6 +131,7 @@ def test_stack_graph_equals_per_layer_graphs():
     per, stack = build(), build()
     graphs = [lay.capture() for lay in per]
     sg = fsvd.fsvd_decoder_stack_capture([lay.desc for lay in stack])
+    ys = []
     try:
         for t in range(N):
             xt = to_dev(xs[t]).reshape(B, 1, cfg.d)
@@ -138,6 +142,7 @@ def test_stack_graph_equals_per_layer_graphs():
             fsvd.fsvd_graph_replay(sg)
             torch.cuda.synchronize()
             assert np.array_equal(bits(per[-1].y), bits(stack[-1].y)), f"step {t}"
+            ys.append(stack[-1].y_host()[:, 0])
         for a, b in zip(per, stack):
             assert np.array_equal(bits(a.k_cache), bits(b.k_cache))
             assert list(b.seqlens.cpu().numpy()) == [L0 + N] * B
@@ -145,3 +150,16 @@ def test_stack_graph_equals_per_layer_graphs():
         for g in graphs:
             fsvd.fsvd_graph_destroy(g)
         fsvd.fsvd_graph_destroy(sg)
+    # the oracle, layer after layer: N decode steps of layer l over the N outputs of layer l-1
+    x_l = xs
+    for l in range(NL):
+        kc, vc = hist[l]
+        x_l, kc_ref, vc_ref, sl = O.decoder_steps(x_l, params[l], cfg, kc, vc, np.full(B, L0))
+        e_k = rel(from_dev(stack[l].k_cache)[:, L0:L0 + N], kc_ref[:, L0:L0 + N])
+        e_v = rel(from_dev(stack[l].v_cache)[:, L0:L0 + N], vc_ref[:, L0:L0 + N])
+        say(f"  layer {l}: appended K {e_k:.2e}  V {e_v:.2e}")
+        assert e_k <= BF16_TOL and e_v <= BF16_TOL
+        assert np.array_equal(bits(stack[l].k_cache)[:, :L0], bits(to_dev(kc))[:, :L0])
+    e_y = rel(np.stack(ys), x_l)
+    say(f"  last layer outputs over {N} steps {e_y:.2e}")
+    assert e_y <= BF16_TOL

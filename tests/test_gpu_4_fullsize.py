@@ -11,8 +11,10 @@
   (MFMA path, eager), then decode steps replayed from the captured graph with the in-graph
   length advance, with the RMSNorm weights folded into A_qkv / A_gu as the benchmark packs
   them.  The oracle runs its own prefill (never the GPU's), with the weights kept separate: the
-  whole K/V cache it writes is compared, the layer output on sampled rows, and the replayed
-  decode outputs.
+  whole K/V cache it writes is compared, the layer output on whole 128-query blocks (first,
+  middle and last of every sequence), and the replayed decode output of every one of the 128
+  steps.
+- The 7B-shaped decode layer at batch 4 over a 16,384-token history (the longest horizon).
 - BERT-Base-shaped encoder layer (768, 12 x 64, d_ff 3072, rank 384), batch 8 x 512: whole output.
 """
 import ctypes
@@ -97,10 +99,16 @@ def test_llama3_8b_gqa_decode_layer_full_b32():
     _decode_case(I.CFG4, "cfg4", 32, L0=8192, pad_tail=0, seed=4)
 
 
+def test_llama7b_decode_layer_history_16384():
+    """The longest decode horizon the stack sweep times: batch 4 over 16,384 cached tokens."""
+    say("llama-7b decode layer, full size, B 4, history 16384")
+    _decode_case(I.CFG2, "cfg2", 4, L0=16384, pad_tail=0, seed=3)
+
+
 def test_llama7b_prefill_then_replayed_decode_full():
-    """4 x 2048 prefill (eager, MFMA path) then 3 graph-replayed decode steps with in-graph advance,
-    exactly as the benchmark drives one layer."""
-    cfg, B, S, ND = I.CFG3, I.CFG3_BATCH, I.CFG3_PREFILL, 3
+    """4 x 2048 prefill (eager, MFMA path) then all 128 graph-replayed decode steps with in-graph
+    advance, exactly as the benchmark drives one layer."""
+    cfg, B, S, ND = I.CFG3, I.CFG3_BATCH, I.CFG3_PREFILL, I.CFG3_DECODE_STEPS
     L_max = S + I.CFG3_DECODE_STEPS
     say("llama-7b prefill", B, "x", S, "then", ND, "replayed decode steps")
     p = I.make_decoder_layer(cfg, B=B, S=S, seed=8, random_norm_weights=True)
@@ -152,26 +160,28 @@ def test_llama7b_prefill_then_replayed_decode_full():
     e_k, e_v = rel(k_gpu, kc_ref[:, :S]), rel(v_gpu, vc_ref[:, :S])
     say(f"  prefill K cache {e_k:.2e}  V cache {e_v:.2e}")
     assert e_k <= BF16_TOL and e_v <= BF16_TOL
-    samples = [(0, 0), (0, 1), (0, 511), (1, 1024), (2, 2046), (3, 2047)]
-    samples += [(int(b), int(s)) for b, s in zip(rng.integers(0, B, 4), rng.integers(0, S, 4))]
+    # whole 128-query blocks (the attention kernel's query tile): the first, a middle and the last
+    # block of every sequence, every row of each
+    QB = 128
     y_ref_rows, y_gpu_rows = [], []
-    for b, s in samples:
-        o = O.attention(q[b:b + 1, s:s + 1], kc_ref[b:b + 1], vc_ref[b:b + 1], [s], causal=True)
-        h = O.lowrank_linear(o.reshape(1, cfg.Hq * cfg.D), p["Ut_o"], p["Vt_o"], residual=p["x"][b, s][None])
-        yr = O.mlp(h, p["mlp_norm_w"], cfg.norm_eps, "swiglu", p["Ut_gate"], p["Vt_gate"], p["Ut_up"], p["Vt_up"],
-                   p["Ut_down"], p["Vt_down"], residual=h)
-        y_ref_rows.append(yr[0])
-        y_gpu_rows.append(y_pre[b, s])
-    e_y = rel(np.stack(y_gpu_rows), np.stack(y_ref_rows))
-    say(f"  prefill output on {len(samples)} sampled rows {e_y:.2e}")
+    for b in range(B):
+        for s0 in (0, S // 2, S - QB):
+            o = O.attention(q[b:b + 1, s0:s0 + QB], kc_ref[b:b + 1], vc_ref[b:b + 1], [s0], causal=True)
+            h = O.lowrank_linear(o.reshape(QB, cfg.Hq * cfg.D), p["Ut_o"], p["Vt_o"], residual=p["x"][b, s0:s0 + QB])
+            yr = O.mlp(h, p["mlp_norm_w"], cfg.norm_eps, "swiglu", p["Ut_gate"], p["Vt_gate"], p["Ut_up"],
+                       p["Vt_up"], p["Ut_down"], p["Vt_down"], residual=h)
+            y_ref_rows.append(yr)
+            y_gpu_rows.append(y_pre[b, s0:s0 + QB])
+    e_y = rel(np.concatenate(y_gpu_rows), np.concatenate(y_ref_rows))
+    say(f"  prefill output on {len(y_ref_rows)} whole {QB}-query blocks {e_y:.2e}")
     assert e_y <= BF16_TOL
 
     # oracle decode steps over the oracle's own prefill caches
-    say("  oracle decode steps ...")
+    say(f"  oracle decode steps ({ND}) ...")
     y_steps, _, _, _ = O.decoder_steps(xs, p, cfg, kc_ref, vc_ref, np.full(B, S))
-    e_d = rel(np.stack(ys), y_steps)
-    say(f"  replayed decode outputs {e_d:.2e}")
-    assert e_d <= BF16_TOL
+    errs = [rel(ys[t], y_steps[t]) for t in range(ND)]
+    say(f"  replayed decode outputs, every step: max {max(errs):.2e} (step {int(np.argmax(errs))})")
+    assert max(errs) <= BF16_TOL
 
 
 def test_bert_base_encoder_layer_full():
