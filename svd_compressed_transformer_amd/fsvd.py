@@ -89,6 +89,11 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"fsvd HIP library not built: {LIB_PATH} is missing (run __graft_entry__.build())")
+        # torch ships its own HIP runtime under the same soname (libamdhip64.so.7) but links it by
+        # file name; loaded first, torch's copy satisfies this library's dependency and the process
+        # has one runtime, so tensors, streams and device state are shared.  Loaded after this
+        # library, torch would bring a second runtime that holds the device on its own.
+        import torch  # noqa: F401
         L = C.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
             f = getattr(L, name)

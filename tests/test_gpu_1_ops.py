@@ -107,11 +107,11 @@ def test_linear_cfg0_fp32():
     assert rel(y, c["x"].astype(np.float64) @ (c["Ut"].T.astype(np.float64) @ c["Vt"].T)) <= F32_TOL
 
 
-@pytest.mark.parametrize("M,K,r,N", [(1, 512, 64, 256), (3, 1000, 40, 1032), (7, 4096, 1640, 520),
+@pytest.mark.parametrize("M,K,r,N", [(1, 512, 64, 256), (3, 1000, 40, 1032), (7, 4096, 1640, 1672),
                                      (16, 2048, 24, 3000), (32, 768, 392, 768), (5, 8, 8, 8),
                                      # 5..32 rows run on the matrix cores: one and two 16-row tiles,
                                      # ragged K, rank and N
-                                     (9, 4096, 1640, 4096), (17, 1000, 40, 1032), (24, 11008, 1640, 520),
+                                     (9, 4096, 1640, 4096), (17, 1000, 40, 1032), (24, 11008, 1640, 1704),
                                      (32, 8, 8, 8)])
 def test_linear_bf16_decode_shapes(M, K, r, N):
     say("bf16 linear", M, K, r, N)
@@ -172,11 +172,12 @@ SMALL = I.scaled_decoder(I.CFG2, d=256, Hq=4, Hkv=2, D=64, d_ff=384,
                          ranks={"q": 100, "k": 36, "v": 20, "o": 64, "gate": 72, "up": 88, "down": 48})
 SMALL128 = I.scaled_decoder(I.CFG4, d=512, Hq=8, Hkv=2, D=128, d_ff=640,
                             ranks={"q": 200, "k": 64, "v": 32, "o": 96, "gate": 80, "up": 120, "down": 72})
-# few heads and output columns over long ranks: at 5..32 rows the matrix-core launches have so few
-# tiles that the reduction is also split over workgroups (partial tiles + a reduce kernel), for the
-# RoPE / cache-append and SwiGLU epilogues too
-SPLIT = I.scaled_decoder(I.CFG2, d=256, Hq=2, Hkv=1, D=64, d_ff=256,
-                         ranks={"q": 1016, "k": 1000, "v": 984, "o": 64, "gate": 1008, "up": 1016, "down": 48})
+# ranks close to the output widths (q 1016 of 1024, k / v ~500 of 512, gate / up ~1000 of 1024):
+# at 5..32 rows the phase-2 matrix-core launches have so few tiles for such long reductions that
+# the reduction is also split over workgroups (partial tiles + a reduce kernel), for the RoPE /
+# cache-append and SwiGLU epilogues too
+SPLIT = I.scaled_decoder(I.CFG2, d=1024, Hq=8, Hkv=4, D=128, d_ff=1024,
+                         ranks={"q": 1016, "k": 504, "v": 496, "o": 64, "gate": 1008, "up": 1016, "down": 48})
 
 
 @pytest.mark.parametrize("cfg,B,S,seqlens", [(SMALL, 2, 1, [5, 0]), (SMALL, 3, 4, [0, 7, 19]),

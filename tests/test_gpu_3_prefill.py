@@ -24,7 +24,7 @@ def say(*a):
 
 
 @pytest.mark.parametrize("M,K,r,N,extras", [(33, 256, 64, 256, False), (300, 1000, 40, 1032, True),
-                                            (1000, 4096, 1640, 520, False), (513, 768, 392, 3000, True),
+                                            (1000, 4096, 1640, 1672, False), (513, 768, 392, 3000, True),
                                             (4096, 768, 384, 768, True)])
 def test_linear_mfma(M, K, r, N, extras):
     say("mfma linear", M, K, r, N, extras)
