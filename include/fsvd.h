@@ -69,7 +69,7 @@ extern "C" {
 
 typedef struct ihipStream_t* fsvd_stream_t; /* a hipStream_t */
 
-#define FSVD_ABI_VERSION 4
+#define FSVD_ABI_VERSION 5
 
 typedef enum {
     FSVD_OK = 0,
@@ -126,7 +126,8 @@ fsvd_status_t fsvd_prepack_colscale(void* dst, int64_t ld_dst, int64_t cols_pad,
  * a2+a3. Fused low-rank linear  [V1] [V15-M1]
  *   y[m, :] = residual[m, :] + bias + (x[m, :] . Ut^T) . Vt^T        (z = x . Ut^T is rank-r)
  * x [M, K] (ldx), Ut [r, K] (ldu), Vt [N, r] (ldv), bias [N] or NULL, residual [M, N] (ldr)
- * or NULL (may alias y for in-place accumulation), y [M, N] (ldy).  dtype FSVD_F32 or FSVD_BF16.
+ * or NULL (may alias y for in-place accumulation), y [M, N] (ldy).  r <= min(K, N) (else
+ * FSVD_ERR_INVALID_ARG).  dtype FSVD_F32 or FSVD_BF16.
  * Decode-sized M (<= 32) runs the HBM-streaming row-dot kernels (z passes through the
  * workspace as a B x r vector; bf16 launches of 5..32 rows also keep a 1.25 MiB slice there for
  * the partial tiles of reductions split across workgroups); larger M runs the bf16 MFMA path
@@ -139,6 +140,29 @@ fsvd_status_t fsvd_lowrank_linear(const void* x, int64_t M, int64_t K, int64_t l
                                   const void* bias, const void* residual, int64_t ldr,
                                   void* y, int64_t ldy, fsvd_dtype_t dtype,
                                   void* ws, size_t ws_bytes, fsvd_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Allocation-free fused low-rank linear, for callers that cannot allocate device memory or
+ * hand the library a workspace: code under hipGraph stream capture, tight serving loops, and
+ * harnesses that forbid allocation.
+ * Same arguments, kernels and result (bit for bit) as fsvd_lowrank_linear without (ws,
+ * ws_bytes): the scratch (the rank-r intermediate z and the split-reduction partials) lives in a
+ * static device array of FSVD_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, held
+ * from the first call on that GPU until the process ends.  A call whose
+ * fsvd_lowrank_linear_ws(M, K, r, N, dtype) exceeds FSVD_NOALLOC_SCRATCH_BYTES returns
+ * FSVD_ERR_WORKSPACE before anything is launched.  The call itself allocates nothing; its first
+ * call on a GPU resolves that GPU's copy of the array once (hipGetSymbolAddress, with the
+ * device current), so make that first call outside stream capture.  Every call on one GPU
+ * shares that GPU's array and finds it as the previous call left it (nothing in it has to start
+ * at zero): calls ordered on one stream are safe; calls that overlap on one GPU (concurrent
+ * streams, unordered host threads) race on it and must not be issued.
+ * ------------------------------------------------------------------------------------------ */
+#define FSVD_NOALLOC_SCRATCH_BYTES (32u << 20) /* 32 MiB per GPU */
+fsvd_status_t fsvd_lowrank_linear_noalloc(const void* x, int64_t M, int64_t K, int64_t ldx,
+                                          const void* Ut, int64_t r, int64_t ldu,
+                                          const void* Vt, int64_t N, int64_t ldv,
+                                          const void* bias, const void* residual, int64_t ldr,
+                                          void* y, int64_t ldy, fsvd_dtype_t dtype, fsvd_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * a2+a3+a5. Packed Q/K/V projection with KV append  [V15-M2] [V15-M3]

@@ -526,27 +526,90 @@ size_t fsvd_lowrank_linear_ws(int64_t M, int64_t K, int64_t r, int64_t N, fsvd_d
     return kWsHeader + align256((size_t)M * r * esize(dtype)) + align256(rowdot_part_bytes(M, dtype));
 }
 
-fsvd_status_t fsvd_lowrank_linear(const void* x, int64_t M, int64_t K, int64_t ldx, const void* Ut, int64_t r,
-                                  int64_t ldu, const void* Vt, int64_t N, int64_t ldv, const void* bias,
-                                  const void* residual, int64_t ldr, void* y, int64_t ldy, fsvd_dtype_t dtype, void* ws,
-                                  size_t ws_bytes, fsvd_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// every argument of a low-rank linear call but the workspace
+fsvd_status_t validate_linear(const void* x, int64_t M, int64_t K, int64_t ldx, const void* Ut, int64_t r, int64_t ldu,
+                              const void* Vt, int64_t N, int64_t ldv, const void* bias, const void* residual,
+                              int64_t ldr, void* y, int64_t ldy, fsvd_dtype_t dtype) {
     TRY(need_dtype(dtype, true));
     TRY(need_dim(M, "M")); TRY(need_dim(K, "K")); TRY(need_dim(r, "r")); TRY(need_dim(N, "N"));
     TRY(need_vec(K, dtype, "K")); TRY(need_vec(r, dtype, "r")); TRY(need_vec(N, dtype, "N"));
     TRY(need_rank(r, K, N, "r"));
-    TRY(need_ptr(x, "x")); TRY(need_ptr(Ut, "Ut")); TRY(need_ptr(Vt, "Vt")); TRY(need_ptr(y, "y")); TRY(need_ptr(ws, "ws"));
+    TRY(need_ptr(x, "x")); TRY(need_ptr(Ut, "Ut")); TRY(need_ptr(Vt, "Vt")); TRY(need_ptr(y, "y"));
     TRY(opt_ptr(bias, "bias")); TRY(opt_ptr(residual, "residual"));
     TRY(need_ld(ldx, K, dtype, "ldx")); TRY(need_ld(ldu, K, dtype, "ldu")); TRY(need_ld(ldv, r, dtype, "ldv"));
     TRY(need_ld(ldy, N, dtype, "ldy"));
     if (residual) TRY(need_ld(ldr, N, dtype, "ldr"));
-    const size_t need = fsvd_lowrank_linear_ws(M, K, r, N, dtype);
-    if (ws_bytes < need) return fail(FSVD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+    return FSVD_OK;
+}
+
+// carves (z, partials) out of a validated workspace and enqueues both phases
+fsvd_status_t run_linear(const void* x, int64_t M, int64_t K, int64_t ldx, const void* Ut, int64_t r, int64_t ldu,
+                         const void* Vt, int64_t N, int64_t ldv, const void* bias, const void* residual, int64_t ldr,
+                         void* y, int64_t ldy, fsvd_dtype_t dtype, void* ws, hipStream_t st) {
     Carve c(ws);
     void* z = c.take((size_t)M * r * esize(dtype));
     float* part = rowdot_part_bytes(M, dtype) ? (float*)c.take(rowdot_part_bytes(M, dtype)) : nullptr;
     LinearBufs lb{z, (int*)ws, part};
     return enqueue_linear(x, (int)M, (int)K, ldx, Ut, (int)r, ldu, Vt, (int)N, ldv, bias, residual, ldr, y, ldy, dtype,
-                          lb, nullptr, 0, 0, (hipStream_t)stream);
+                          lb, nullptr, 0, 0, st);
+}
+
+// Scratch of the allocation-free linear: one copy per GPU, resident until the process ends.  In
+// host code `scratch` only names the symbol; its device address on each GPU comes from
+// hipGetSymbolAddress (resolved once per device, with that device current) and is what the
+// kernels receive.
+static __device__ __align__(256) unsigned char scratch[FSVD_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+fsvd_status_t scratch_on_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FSVD_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(FSVD_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(FSVD_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return FSVD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fsvd_status_t fsvd_lowrank_linear(const void* x, int64_t M, int64_t K, int64_t ldx, const void* Ut, int64_t r,
+                                  int64_t ldu, const void* Vt, int64_t N, int64_t ldv, const void* bias,
+                                  const void* residual, int64_t ldr, void* y, int64_t ldy, fsvd_dtype_t dtype, void* ws,
+                                  size_t ws_bytes, fsvd_stream_t stream) {
+    TRY(validate_linear(x, M, K, ldx, Ut, r, ldu, Vt, N, ldv, bias, residual, ldr, y, ldy, dtype));
+    TRY(need_ptr(ws, "ws"));
+    const size_t need = fsvd_lowrank_linear_ws(M, K, r, N, dtype);
+    if (ws_bytes < need) return fail(FSVD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+    return run_linear(x, M, K, ldx, Ut, r, ldu, Vt, N, ldv, bias, residual, ldr, y, ldy, dtype, ws, (hipStream_t)stream);
+}
+
+fsvd_status_t fsvd_lowrank_linear_noalloc(const void* x, int64_t M, int64_t K, int64_t ldx, const void* Ut, int64_t r,
+                                          int64_t ldu, const void* Vt, int64_t N, int64_t ldv, const void* bias,
+                                          const void* residual, int64_t ldr, void* y, int64_t ldy, fsvd_dtype_t dtype,
+                                          fsvd_stream_t stream) {
+    TRY(validate_linear(x, M, K, ldx, Ut, r, ldu, Vt, N, ldv, bias, residual, ldr, y, ldy, dtype));
+    const size_t need = fsvd_lowrank_linear_ws(M, K, r, N, dtype);
+    if (need > (size_t)FSVD_NOALLOC_SCRATCH_BYTES)
+        return fail(FSVD_ERR_WORKSPACE, "this call needs %zu bytes of scratch, above the %zu-byte static scratch", need,
+                    (size_t)FSVD_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    TRY(scratch_on_current_device(&ws));
+    return run_linear(x, M, K, ldx, Ut, r, ldu, Vt, N, ldv, bias, residual, ldr, y, ldy, dtype, ws, (hipStream_t)stream);
 }
 
 size_t fsvd_lowrank_qkv_ws(int64_t B, int64_t S, int64_t d, int64_t r_q, int64_t r_k, int64_t r_v, int64_t Hq,

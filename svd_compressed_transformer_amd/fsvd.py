@@ -50,6 +50,8 @@ _SIGS = {
     "fsvd_lowrank_linear_ws": (_sz, [_i64, _i64, _i64, _i64, C.c_int]),
     "fsvd_lowrank_linear": (C.c_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64,
                                       _vp, _i64, C.c_int, _vp, _sz, _vp]),
+    "fsvd_lowrank_linear_noalloc": (C.c_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp,
+                                              _i64, _vp, _i64, C.c_int, _vp]),
     "fsvd_lowrank_qkv_ws": (_sz, [_i64] * 9),
     "fsvd_lowrank_qkv": (C.c_int, [_vp, _i64, _i64, _i64, _vp, _f32, _vp, _i64, _i64, _i64, _vp, _vp, _vp,
                                    _i64, _i64, _i64, _f32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, C.c_int, _vp, _sz,
@@ -176,6 +178,16 @@ def fsvd_lowrank_linear(x, M, K, ldx, Ut, r, ldu, Vt, N, ldv, bias, residual, ld
                         stream=None):
     _check(lib().fsvd_lowrank_linear(_p(x), M, K, ldx, _p(Ut), r, ldu, _p(Vt), N, ldv, _p(bias), _p(residual), ldr,
                                      _p(y), ldy, dtype, _p(ws), ws_bytes, _s(stream)))
+
+
+def fsvd_lowrank_linear_noalloc(x, M, K, ldx, Ut, r, ldu, Vt, N, ldv, bias, residual, ldr, y, ldy, dtype,
+                                stream=None):
+    """fsvd_lowrank_linear with the library's static per-GPU scratch instead of a workspace."""
+    _check(lib().fsvd_lowrank_linear_noalloc(_p(x), M, K, ldx, _p(Ut), r, ldu, _p(Vt), N, ldv, _p(bias),
+                                             _p(residual), ldr, _p(y), ldy, dtype, _s(stream)))
+
+
+FSVD_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def fsvd_lowrank_qkv_ws(B, S, d, r_q, r_k, r_v, Hq, Hkv, D) -> int:
