@@ -69,7 +69,7 @@ extern "C" {
 
 typedef struct ihipStream_t* fsvd_stream_t; /* a hipStream_t */
 
-#define FSVD_ABI_VERSION 5
+#define FSVD_ABI_VERSION 6
 
 typedef enum {
     FSVD_OK = 0,
@@ -337,6 +337,10 @@ typedef struct fsvd_decoder_layer_desc {
     int32_t* cache_seqlens;                     /* [B] */
     void* ws;
     size_t ws_bytes;
+    /* S > 1 (prefill): the B * S token rows pass through the layer in ceil(B * S / prefill_chunk)
+     * passes of nearly equal size, so the workspace holds one pass and does not grow with the
+     * sequence; 0 -> 8192 rows, else at least 256.  The result does not depend on it. */
+    int64_t prefill_chunk;
 } fsvd_decoder_layer_desc;
 
 typedef struct fsvd_graph fsvd_graph; /* opaque */

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma(const AttnArgs a) {
     const int bh = blockIdx.x % bh_count;
     const int h = bh % a.Hq, b = bh / a.Hq;
     const int g = (h * a.Hkv) / a.Hq;
-    const int64_t base = a.seqlens[b];
+    const int64_t base = (int64_t)a.seqlens[b] + a.pos_off;
 
     int64_t kend = a.causal ? base + min(a.Sq, qt * BQW + BQW) : base + a.Sq;
     if (kend > a.L_max) {

@@ -160,6 +160,8 @@ struct QkvDims {
     int B, S, d, rq, rk, rv, Hq, Hkv, D;
     int64_t L_max;
     float eps, theta;
+    int rows;     // token rows of this launch (0: all B * S)
+    int row_off;  // first token row of this launch within the call's [B, S] tokens
 };
 struct QkvBufs {
     void* z;       // [M, rq+rk+rv] bf16
@@ -179,9 +181,10 @@ size_t qkv_scratch(int64_t M, int64_t d, int64_t rtot) {
 fsvd_status_t enqueue_qkv(const QkvDims& q, const void* x, bool norm, const void* norm_w, const void* A, const void* Vq,
                           const void* Vk, const void* Vv, void* q_out, void* kc, void* vc, const int32_t* seqlens,
                           void* k_out, void* v_out, const QkvBufs& wb, hipStream_t st) {
-    const int M = q.B * q.S;
+    const int M = q.rows > 0 ? q.rows : q.B * q.S;
     const int rtot = q.rq + q.rk + q.rv;
     if (M <= kRowdotMaxM) {
+        if (q.row_off != 0) return fail(FSVD_ERR_UNSUPPORTED, "row-dot Q/K/V launch with a row offset");
         RowdotArgs a{};
         a.nseg = 1;
         a.act = x; a.lda = q.d; a.M = M; a.err = wb.err;
@@ -228,7 +231,8 @@ fsvd_status_t enqueue_qkv(const QkvDims& q, const void* x, bool norm, const void
         h.Bm = (const bf16_t*)Vs[i]; h.ldb = rs[i];
         h.M = M; h.N = Ns[i]; h.K = rs[i];
         h.S = q.S; h.Hq = q.Hq; h.Hkv = q.Hkv; h.D = q.D; h.rope_theta = q.theta; h.L_max = q.L_max;
-        h.seqlens = seqlens; h.q_out = (bf16_t*)q_out; h.k_cache = (bf16_t*)kc; h.v_cache = (bf16_t*)vc;
+        h.seqlens = seqlens; h.row_off = q.row_off;
+        h.q_out = (bf16_t*)q_out; h.k_cache = (bf16_t*)kc; h.v_cache = (bf16_t*)vc;
         h.k_out = (bf16_t*)k_out; h.v_out = (bf16_t*)v_out;
         h.seg = i;
         h.err = wb.err;
@@ -340,6 +344,7 @@ fsvd_status_t check_attn_shape(int64_t Hq, int64_t Hkv, int64_t D) {
 
 struct LayerPlan {
     size_t bytes;
+    int64_t chunk;   // token rows per pass through the layer (prefill); M at decode sizes
     void *q, *o, *h;
     QkvBufs qb;
     float* attn_part;
@@ -349,30 +354,64 @@ struct LayerPlan {
     float* part;
 };
 
+constexpr int64_t kPrefillChunk = 8192;   // default rows per prefill pass
+constexpr int64_t kMinPrefillChunk = 256;
+
+// Rows per prefill pass: the call's M = B * S tokens run in ceil(M / limit) passes of nearly equal
+// size (each at least limit / 2 rows, so never a row-dot-sized pass).
+int64_t prefill_chunk_rows(const fsvd_decoder_layer_desc* d) {
+    const int64_t M = d->B * d->S;
+    const int64_t lim = d->prefill_chunk > 0 ? d->prefill_chunk : kPrefillChunk;
+    const int64_t n = (M + lim - 1) / lim;
+    return (M + n - 1) / n;
+}
+
 LayerPlan plan_layer(const fsvd_decoder_layer_desc* d, void* ws) {
     LayerPlan p{};
     Carve c(ws);
     const int64_t M = d->B * d->S;
     const int64_t qd = d->Hq * d->D;
+    if (M > kRowdotMaxM) {
+        // Prefill: one pass per chunk of Mc token rows; the workspace holds one chunk, so it does
+        // not grow with the sequence.  Buffers share two slots by liveness (each one is dead
+        // before the next one in its slot is written):
+        //   slot A: z_qkv (Q/K/V phase 1 -> 2), o (attention -> O phase 1), z_gu (gate|up
+        //           phase 1 -> 2), z_d (down phase 1 -> 2)
+        //   slot B: xn (RMSNorm -> Q/K/V phase 1), q (phase 2 -> attention), z_o (O phase 1 -> 2),
+        //           xn (RMSNorm -> gate|up phase 1), t (gate|up phase 2 -> down phase 1)
+        // plus h (O output, MLP input and residual; live to the end) and the per-row rstd.
+        const int64_t Mc = prefill_chunk_rows(d);
+        p.chunk = Mc;
+        const int64_t rtot = d->r_q + d->r_k + d->r_v, rgu = d->r_g + d->r_u;
+        const int64_t wa = std::max(std::max(rtot, qd), std::max(rgu, d->r_d));
+        const int64_t wb = std::max(std::max(qd, d->r_o), std::max(d->d_ff, d->d));
+        p.h = c.take((size_t)Mc * d->d * 2);
+        void* sa = c.take((size_t)Mc * wa * 2);
+        void* sb = c.take((size_t)Mc * wb * 2);
+        float* rstd = (float*)c.take((size_t)Mc * 4);
+        p.qb.z = sa; p.qb.xn = sb; p.qb.rstd = rstd;
+        p.q = sb;
+        p.o = sa;
+        p.z_o = sb;
+        p.mb.xn = sb; p.mb.rstd = rstd; p.mb.z_gu = sa; p.mb.t = sb; p.mb.z_d = sa;
+        int* err = ws ? (int*)ws : nullptr;
+        p.qb.err = err;
+        p.mb.err = err;
+        p.bytes = c.off;
+        return p;
+    }
+    p.chunk = M;
     p.q = c.take((size_t)M * qd * 2);
     p.o = c.take((size_t)M * qd * 2);
     p.h = c.take((size_t)M * d->d * 2);
     const int64_t rtot = d->r_q + d->r_k + d->r_v;
     p.qb.z = c.take((size_t)M * rtot * 2);
-    if (M > kRowdotMaxM) {
-        p.qb.xn = c.take((size_t)M * d->d * 2);
-        p.qb.rstd = (float*)c.take((size_t)M * 4);
-    }
     p.nsplit = attn_default_splits((int)d->B, (int)d->Hkv, d->L_max);
     p.attn_part = (float*)c.take(attn_decode_ws_bytes((int)d->B, (int)d->Hq, (int)d->D, p.nsplit));
     p.z_o = c.take((size_t)M * d->r_o * 2);
     p.mb.z_gu = c.take((size_t)M * (d->r_g + d->r_u) * 2);
     p.mb.t = c.take((size_t)M * d->d_ff * 2);
     p.mb.z_d = c.take((size_t)M * d->r_d * 2);
-    if (M > kRowdotMaxM) {
-        p.mb.xn = p.qb.xn;   // the qkv normalised input is dead by the time the MLP runs
-        p.mb.rstd = p.qb.rstd;
-    }
     if (rowdot_part_bytes(M, FSVD_BF16)) {  // one partials slice, used by one launch at a time
         p.part = (float*)c.take(rowdot_part_bytes(M, FSVD_BF16));
         p.qb.part = p.part;
@@ -414,9 +453,43 @@ fsvd_status_t validate_layer(const fsvd_decoder_layer_desc* d) {
     if (!d->cache_seqlens) return fail(FSVD_ERR_INVALID_ARG, "cache_seqlens is NULL");
     if (d->x == d->y) return fail(FSVD_ERR_INVALID_ARG, "y must not alias x");
     if (d->S > d->L_max) return fail(FSVD_ERR_INVALID_ARG, "S (%lld) exceeds L_max", (long long)d->S);
+    if (d->prefill_chunk != 0 && (d->prefill_chunk < kMinPrefillChunk || d->prefill_chunk > ((int64_t)1 << 30)))
+        return fail(FSVD_ERR_INVALID_ARG, "prefill_chunk = %lld: 0 (default) or %lld .. 2^30 rows",
+                    (long long)d->prefill_chunk, (long long)kMinPrefillChunk);
     const LayerPlan p = plan_layer(d, nullptr);
     if (d->ws_bytes < p.bytes)
         return fail(FSVD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", d->ws_bytes, p.bytes);
+    return FSVD_OK;
+}
+
+// Attention of token rows [r0, r0 + rows) of a prefill call (queries at q, outputs at out, both
+// [rows, Hq, D]) over the dense cache: one launch per run of whole sequences, one per partial
+// sequence, each query at position cache_seqlens[b] + s.
+fsvd_status_t enqueue_attn_rows(const fsvd_decoder_layer_desc* d, const bf16_t* q, bf16_t* out, int64_t r0,
+                                int64_t rows, int* err, hipStream_t st) {
+    const int64_t S = d->S, qd = d->Hq * d->D, kv_seq = d->L_max * d->Hkv * d->D;
+    int64_t r = r0;
+    const int64_t r1 = r0 + rows;
+    while (r < r1) {
+        const int64_t b = r / S, s0 = r - b * S;
+        int64_t nseq = 1, len;
+        if (s0 == 0 && r + S <= r1) {  // whole sequences b .. b + nseq - 1
+            nseq = (r1 - r) / S;
+            len = S;
+        } else {
+            len = std::min(S - s0, r1 - r);
+        }
+        AttnArgs a{};
+        a.q = q + (r - r0) * qd; a.out = out + (r - r0) * qd;
+        a.kc = (const bf16_t*)d->k_cache + b * kv_seq; a.vc = (const bf16_t*)d->v_cache + b * kv_seq;
+        a.seqlens = d->cache_seqlens + b;
+        a.B = (int)nseq; a.Sq = (int)len; a.Hq = (int)d->Hq; a.Hkv = (int)d->Hkv; a.D = (int)d->D;
+        a.L_max = d->L_max; a.pos_off = (int)s0;
+        a.scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf((float)d->D);
+        a.causal = 1; a.err = err;
+        TRY(launch_attn_prefill(a, st));
+        r += nseq * len;
+    }
     return FSVD_OK;
 }
 
@@ -424,8 +497,35 @@ fsvd_status_t enqueue_layer(const fsvd_decoder_layer_desc* d, hipStream_t st) {
     const LayerPlan p = plan_layer(d, d->ws);
     const int B = (int)d->B, S = (int)d->S, M = B * S;
     QkvDims qd{B, S, (int)d->d, (int)d->r_q, (int)d->r_k, (int)d->r_v, (int)d->Hq, (int)d->Hkv, (int)d->D,
-               d->L_max, d->norm_eps, d->rope_theta};
+               d->L_max, d->norm_eps, d->rope_theta, 0, 0};
     const bool folded = (d->flags & FSVD_LAYER_NORM_FOLDED) != 0;
+    if (M > kRowdotMaxM) {
+        // prefill: passes of p.chunk token rows; the lengths advance once, after the last pass
+        const int qdim = (int)(d->Hq * d->D);
+        const int64_t nchunk = (M + p.chunk - 1) / p.chunk;
+        for (int64_t c = 0; c < nchunk; ++c) {
+            const int64_t r0 = c * M / nchunk, r1 = (c + 1) * M / nchunk, mc = r1 - r0;
+            const bf16_t* xc = (const bf16_t*)d->x + r0 * d->d;
+            bf16_t* yc = (bf16_t*)d->y + r0 * d->d;
+            QkvDims qc = qd;
+            qc.rows = (int)mc;
+            qc.row_off = (int)r0;
+            TRY(enqueue_qkv(qc, xc, folded || d->attn_norm_w != nullptr, folded ? nullptr : d->attn_norm_w, d->A_qkv,
+                            d->Vt_q, d->Vt_k, d->Vt_v, p.q, d->k_cache, d->v_cache, d->cache_seqlens, nullptr,
+                            nullptr, p.qb, st));
+            TRY(enqueue_attn_rows(d, (const bf16_t*)p.q, (bf16_t*)p.o, r0, mc, p.qb.err, st));
+            LinearBufs lb{p.z_o, p.qb.err, nullptr};
+            TRY(enqueue_linear(p.o, (int)mc, qdim, qdim, d->Ut_o, (int)d->r_o, qdim, d->Vt_o, (int)d->d, d->r_o,
+                               nullptr, xc, d->d, p.h, d->d, FSVD_BF16, lb, nullptr, 0, 0, st));
+            MlpDims md{(int)mc, (int)d->d, (int)d->r_g, (int)d->r_u, (int)d->d_ff, (int)d->r_d, d->norm_eps,
+                       FSVD_ACT_SWIGLU};
+            const bool last = c + 1 == nchunk;
+            TRY(enqueue_mlp(md, p.h, folded || d->mlp_norm_w != nullptr, folded ? nullptr : d->mlp_norm_w, d->A_gu,
+                            d->Vt_g, d->Vt_u, d->Ut_d, d->Vt_d, p.h, yc, p.mb,
+                            (last && d->advance_seqlens) ? d->cache_seqlens : nullptr, B, S, st));
+        }
+        return FSVD_OK;
+    }
     TRY(enqueue_qkv(qd, d->x, folded || d->attn_norm_w != nullptr, folded ? nullptr : d->attn_norm_w, d->A_qkv, d->Vt_q, d->Vt_k, d->Vt_v, p.q, d->k_cache, d->v_cache,
                     d->cache_seqlens, nullptr, nullptr, p.qb, st));
     TRY(enqueue_attn(p.q, d->k_cache, d->v_cache, d->L_max, d->cache_seqlens, B, S, (int)d->Hq, (int)d->Hkv,
@@ -649,7 +749,8 @@ fsvd_status_t fsvd_lowrank_qkv(const void* x, int64_t B, int64_t S, int64_t d, c
     }
     if (rowdot_part_bytes(M, FSVD_BF16)) qb.part = (float*)c.take(rowdot_part_bytes(M, FSVD_BF16));
     qb.err = (int*)ws;
-    QkvDims qd{(int)B, (int)S, (int)d, (int)r_q, (int)r_k, (int)r_v, (int)Hq, (int)Hkv, (int)D, L_max, norm_eps, rope_theta};
+    QkvDims qd{(int)B, (int)S, (int)d, (int)r_q, (int)r_k, (int)r_v, (int)Hq, (int)Hkv, (int)D, L_max, norm_eps, rope_theta,
+               0, 0};
     return enqueue_qkv(qd, x, norm_w != nullptr, norm_w, A_qkv, Vt_q, Vt_k, Vt_v, q_out, k_cache, v_cache, cache_seqlens, k_out, v_out, qb,
                        (hipStream_t)stream);
 }

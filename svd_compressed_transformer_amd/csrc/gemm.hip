@@ -345,7 +345,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
             const int row = m0 + r;
             int64_t pp = 0, dr = -1;
             if (row < g.M) {
-                const int b = row / g.S, s = row - b * g.S;
+                const int grow = g.row_off + row;  // token index within the call
+                const int b = grow / g.S, s = grow - b * g.S;
                 pp = (g.seqlens ? (int64_t)g.seqlens[b] : 0) + s;
                 if (g.seg == 0) dr = (int64_t)row * g.N;
                 else if (pp >= 0 && pp < g.L_max) dr = ((int64_t)b * g.L_max + pp) * g.N;

@@ -89,6 +89,8 @@ struct AttnArgs {
     int nsplit;        // decode: partitions of the length
     float* part;       // decode partials [B, Hq, nsplit, D + 2]
     int* err;
+    int pos_off;       // Sq > 1: query s of sequence b sits at position seqlens[b] + pos_off + s (a
+                       // prefill chunk that starts pos_off tokens into the call's new tokens)
 };
 // factorised attention: S tokens per sequence among themselves, Q/K/V rebuilt from z on chip
 struct FactAttnArgs {
@@ -142,6 +144,8 @@ struct GemmArgs {
     float rope_theta;
     int64_t L_max;
     const int32_t* seqlens;      // GEPI_QKV: position of row (b, s) = seqlens[b] + s (NULL: s)
+    int row_off;                 // GEPI_QKV: row m of this launch is token row_off + m of the call
+                                 // ([B, S] flattened: b = (row_off + m) / S); q_out keeps local rows
     float* C32;                  // GEPI_ACC32: fp32 accumulator [M, ldc]
     bf16_t *q_out, *k_cache, *v_cache, *k_out, *v_out;
     int* err;

@@ -38,7 +38,7 @@ class DecoderLayerDesc(C.Structure):
         ("advance_seqlens", _i32), ("flags", _i32)] + [
         (n, _vp) for n in ("x", "y", "attn_norm_w", "mlp_norm_w", "A_qkv", "Vt_q", "Vt_k", "Vt_v", "Ut_o", "Vt_o",
                            "A_gu", "Vt_g", "Vt_u", "Ut_d", "Vt_d", "k_cache", "v_cache", "cache_seqlens", "ws")] + [
-        ("ws_bytes", _sz)]
+        ("ws_bytes", _sz), ("prefill_chunk", _i64)]
 
 
 _SIGS = {

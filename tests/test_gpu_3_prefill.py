@@ -124,6 +124,36 @@ def test_decoder_prefill_layer(fold):
     assert rel(from_dev(lay.k_cache), kc_ref) <= BF16_TOL
 
 
+@pytest.mark.parametrize("chunk,fold", [(256, False), (512, True), (1024, False)])
+def test_decoder_prefill_layer_chunked(chunk, fold):
+    """The prefill passes through the layer in chunks of token rows (the workspace holds one
+    chunk): with 900 rows over 3 sequences of 300, chunk 256 runs 4 passes of 225 rows and 512
+    runs 2 of 450, so passes start and end inside sequences and span sequence boundaries; 1024 is
+    one pass.  Output, the whole K/V cache and the length advance against the oracle."""
+    cfg = SMALL
+    B, S, L_max = 3, 300, 340
+    sl0 = [0, 17, 40]
+    say("decoder prefill layer, chunk", chunk, "folded" if fold else "")
+    p = I.make_decoder_layer(cfg, B=B, S=S, seed=91, random_norm_weights=True)
+    lay = DeviceLayer(cfg, p, B=B, S=S, L_max=L_max, kc=None, vc=None, seqlens=sl0, fold_norm=fold, advance=True)
+    full_ws = lay.ws.numel()
+    lay.desc.prefill_chunk = chunk
+    nb = fsvd.fsvd_decoder_layer_ws(lay.desc)
+    if chunk < B * S:
+        assert nb < full_ws, (nb, full_ws)
+    ws = fsvd.workspace(nb)
+    lay.desc.ws, lay.desc.ws_bytes = ws.data_ptr(), ws.numel()
+    lay.run()
+    torch.cuda.synchronize()
+    assert fsvd.fsvd_poll_device_error(ws) == 0
+    assert list(from_dev(lay.seqlens).astype(int)) == [v + S for v in sl0]
+    z = np.zeros((B, L_max, cfg.Hkv, cfg.D))
+    y_ref, kc_ref, vc_ref = O.decoder_layer(p["x"], p, cfg, z, z, sl0)
+    e_y, e_k, e_v = rel(lay.y_host(), y_ref), rel(from_dev(lay.k_cache), kc_ref), rel(from_dev(lay.v_cache), vc_ref)
+    say(f"  workspace {nb} B (one pass of all rows: {full_ws} B); y {e_y:.2e} K {e_k:.2e} V {e_v:.2e}")
+    assert e_y <= BF16_TOL and e_k <= BF16_TOL and e_v <= BF16_TOL
+
+
 def encoder_forward(cfg, p, B, S):
     """BERT-style post-norm layer composed from the C-ABI calls (qkv without norm/RoPE into a
     fresh K/V buffer, non-causal attention, O with residual, LayerNorm, GELU MLP with residual,
