@@ -81,6 +81,21 @@ def layer_flops_prefill(cfg, M, r):
     return proj
 
 
+def attn_flops_prefill(cfg, B, S):
+    """Causal attention of S tokens per sequence: q.k and p.v over the keys each query sees."""
+    return 4 * B * cfg.Hq * cfg.D * (S * (S + 1) // 2)
+
+
+def unfused_prefill_bytes(cfg, B, S, r):
+    """Activation bytes an unfused low-rank prefill layer would hold (bf16, scores fp32): layer I/O,
+    the normalised inputs, z of every projection, q, o, h, g, u, t and the naive attention scores."""
+    M = B * S
+    qd = cfg.Hq * cfg.D
+    z = M * (r["q"] + r["k"] + r["v"] + r["o"] + r["gate"] + r["up"] + r["down"])
+    return 2 * (2 * M * cfg.d + 2 * M * cfg.d + z + 2 * M * qd + M * cfg.d + 3 * M * cfg.d_ff) + \
+        4 * B * cfg.Hq * S * S
+
+
 def recorded_traffic():
     """Measured HBM bytes per decode-attention call, or None when no summary exists or the kernel
     source changed since the counters were taken."""
@@ -101,43 +116,93 @@ def recorded_traffic():
 # ----------------------------------------------------------------------------- CPU oracle baseline
 
 
-def cpu_baseline(cfg, budget_s=20.0):
-    """The fp64 oracle, as it stands, on a bounded sample of the same workload: one layer,
-    prefill of one 256-token sequence, then decode steps of batch 4 over a 2048-token history
-    until the time budget is used.  Returns layer-tokens/s and what was run."""
-    from oracle import fsvd_oracle as O
-    from svd_compressed_transformer_amd import inputs as I
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1]), \
+            ",".join(sorted({i.get("internal_api", "?") for i in threadpool_info()}))
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
-    p = I.make_decoder_layer(cfg, B=1, S=256, seed=100)
-    L_max = 2048 + 128
-    t0 = time.perf_counter()
-    z = np.zeros((1, 256, cfg.Hkv, cfg.D))
-    O.decoder_layer(p["x"], p, cfg, z, z, np.zeros(1, dtype=np.int64))
-    t_pre = time.perf_counter() - t0
-    tokens = 256
-    kc, vc = I.make_kv_history(4, L_max, cfg.Hkv, cfg.D, 2048, seed=101)
-    pd = dict(p)
+        return len(os.sched_getaffinity(0)), "?"
+
+
+def _median_rate(fn, runs=3):
+    """Median over runs of (work units, seconds) -> units/s."""
+    rates = []
+    for _ in range(runs):
+        units, sec = fn()
+        rates.append(units / sec)
+    return float(np.median(rates))
+
+
+def cpu_baseline(cfg, prefill_tokens_per_layer, decode_tokens_per_layer):
+    """The fp64 oracle, as it stands, on bounded samples of the benchmark's own units, on this
+    host's cores: the prefill of one 256-token sequence through one full-size layer (tokens/s per
+    layer) and batch-4 decode layer-steps over a 2048-token history (tokens/s per layer), each the
+    median of 3 runs; plus single-thread figures for the fp32 linear (x 16 x 256, rank 64) and one
+    batch-1 decode layer-step.  ``value`` is the step's mix of prefill and decode tokens (the GPU
+    line's unit) at those two rates."""
+    from oracle import fsvd_oracle as O
+    from svd_compressed_transformer_amd import inputs as I
+    threads, blas = _blas_threads()
+    t_all = time.perf_counter()
+    S_pre = 256
+    p = I.make_decoder_layer(cfg, B=1, S=S_pre, seed=100)
+    z = np.zeros((1, S_pre, cfg.Hkv, cfg.D))
+
+    def prefill():
+        t0 = time.perf_counter()
+        O.decoder_layer(p["x"], p, cfg, z, z, np.zeros(1, dtype=np.int64))
+        return S_pre, time.perf_counter() - t0
+
+    r_pre = _median_rate(prefill)
+    B, L = 4, 2048
+    kc, vc = I.make_kv_history(B, L + 8, cfg.Hkv, cfg.D, L, seed=101)
     rng = np.random.default_rng(102)
-    sl = np.full(4, 2048)
-    t1 = time.perf_counter()
-    nsteps = 0
-    while True:
-        x = I.round_bf16(rng.standard_normal((4, 1, cfg.d)))
-        _, kc, vc = O.decoder_layer(x, pd, cfg, kc, vc, sl)
-        sl = sl + 1
-        nsteps += 1
-        if time.perf_counter() - t0 > budget_s or nsteps >= 96:
-            break
-    t_dec = time.perf_counter() - t1
-    total = t_pre + t_dec
-    tokens += 4 * nsteps
-    return {"value": tokens / total, "unit": "tokens/s per layer", "cores": int(threads), "kind": "oracle",
-            "sample": f"1 layer: prefill 1x256 tokens ({t_pre:.1f} s) + {nsteps} decode steps at batch 4, "
-                      f"history 2048 ({t_dec:.1f} s); numpy fp64"}
+    xs = [I.round_bf16(rng.standard_normal((B, 1, cfg.d))) for _ in range(4)]
+
+    def decode():
+        sl = np.full(B, L)
+        k, v = kc, vc
+        t0 = time.perf_counter()
+        for x in xs:
+            _, k, v = O.decoder_layer(x, p, cfg, k, v, sl)
+            sl = sl + 1
+        return B * len(xs), time.perf_counter() - t0
+
+    r_dec = _median_rate(decode)
+    # single thread: the fp32 linear and one batch-1 decode layer-step
+    single = {}
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            c = I.make_linear_case(I.CFG0)
+
+            def lin():
+                t0 = time.perf_counter()
+                for _ in range(200):
+                    O.lowrank_linear(c["x"], c["Ut"], c["Vt"])
+                return 200, time.perf_counter() - t0
+
+            single["linear_fp32_calls_per_s"] = round(_median_rate(lin), 1)
+
+            def dec1():
+                t0 = time.perf_counter()
+                O.decoder_layer(xs[0][:1], p, cfg, kc[:1], vc[:1], np.full(1, L))
+                return 1, time.perf_counter() - t0
+
+            single["decode_b1_tokens_per_s_per_layer"] = round(_median_rate(dec1), 3)
+    except Exception as e:  # pragma: no cover
+        single["error"] = str(e)
+    t_step = prefill_tokens_per_layer / r_pre + decode_tokens_per_layer / r_dec
+    value = (prefill_tokens_per_layer + decode_tokens_per_layer) / t_step
+    return {"value": round(value, 3), "unit": "tokens/s per layer", "cores": int(threads), "kind": "oracle",
+            "blas": blas,
+            "prefill_tokens_per_s_per_layer": round(r_pre, 2), "decode_tokens_per_s_per_layer": round(r_dec, 3),
+            "single_thread": single,
+            "sample": f"numpy fp64 oracle, one full-size layer: prefill of 1 x {S_pre} tokens and 4 decode "
+                      f"steps at batch 4 over history {L}, median of 3 runs each; value = the benchmark step's "
+                      f"mix ({prefill_tokens_per_layer} prefill + {decode_tokens_per_layer} decode tokens per layer) "
+                      f"at those rates; {time.perf_counter() - t_all:.1f} s of CPU work"}
 
 
 # ----------------------------------------------------------------------------- GPU run
@@ -305,15 +370,119 @@ def main():
     t_dec_stack_ms = ea.elapsed_time(eb)
     fsvd.fsvd_graph_destroy(stack_g)
 
+    # ------------------------------------------------ prefill attention, timed live
+    # The causal attention of the prefill (the MFMA attention kernel over each layer's cache), so the
+    # projections' share of the prefill time and the whole prefill's flops can be reported apart.
+    qp = torch.empty((B, S, cfg.Hq, cfg.D), dtype=torch.bfloat16, device=dev).normal_()
+    op = torch.empty_like(qp)
+    sl0 = torch.zeros((B,), dtype=torch.int32, device=dev)
+    pa_ws = fsvd.workspace(fsvd.fsvd_decode_attn_dense_kv_ws(B, S, cfg.Hq, cfg.Hkv, cfg.D, L_max), device=dev)
+
+    def prefill_attn(l):
+        fsvd.fsvd_decode_attn_dense_kv(qp, kcs[l], vcs[l], L_max, sl0, B, S, cfg.Hq, cfg.Hkv, cfg.D, 0.0, 1, op,
+                                       fsvd.FSVD_BF16, pa_ws, pa_ws.numel(), stream)
+
+    for l in range(NL):
+        prefill_attn(l)
+    ea.record(stream)
+    for rep in range(3):
+        for l in range(NL):
+            prefill_attn(l)
+    eb.record(stream)
+    torch.cuda.synchronize()
+    t_pattn_ms = ea.elapsed_time(eb) / 3  # per stack pass (NL layers)
+    del qp, op
+
+    # ------------------------------------------------ peak activation bytes (torch's allocator)
+    # Everything one prefill layer call holds beyond its inputs, weights and KV cache: the
+    # workspace the call needs and its output, from the allocator's peak across the call; at the
+    # default pass size (the whole 4 x 2048 prefill in one pass) and at 2048-row passes, with the
+    # 2048-row passes also timed over the stack.
+    def one_layer_peak(chunk):
+        d = type(layers_pre[0].desc)()
+        ctypes.memmove(ctypes.addressof(d), ctypes.addressof(layers_pre[0].desc), ctypes.sizeof(d))
+        d.prefill_chunk = chunk
+        d.advance_seqlens = 0
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats(dev)
+        base = torch.cuda.memory_allocated(dev)
+        ws = fsvd.workspace(fsvd.fsvd_decoder_layer_ws(d), device=dev)
+        y = torch.empty((B, S, cfg.d), dtype=torch.bfloat16, device=dev)
+        d.ws, d.ws_bytes, d.y = ws.data_ptr(), ws.numel(), y.data_ptr()
+        sl_all[0].zero_()
+        fsvd.fsvd_decoder_layer_run(d, stream)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated(dev) - base
+        return {"chunk_rows": chunk or 8192, "allocator_peak": int(peak), "workspace": int(ws.numel())}
+
+    act = {"cfg3_prefill_layer": one_layer_peak(0), "cfg3_prefill_layer_chunk2048": one_layer_peak(2048)}
+    act["unfused_count_cfg3"] = int(unfused_prefill_bytes(cfg, B, S, logical))
+    # the 2048-row passes over the whole stack: time against the default
+    ws2 = fsvd.workspace(act["cfg3_prefill_layer_chunk2048"]["workspace"], device=dev)
+    saved = [(pre.desc.prefill_chunk, pre.desc.ws, pre.desc.ws_bytes) for pre in layers_pre]
+    for pre in layers_pre:
+        pre.desc.prefill_chunk = 2048
+        pre.desc.ws, pre.desc.ws_bytes = ws2.data_ptr(), ws2.numel()
+    t_chunk = []
+    for rep in range(3):
+        sl_all.zero_()
+        ea.record(stream)
+        for pre in layers_pre:
+            fsvd.fsvd_decoder_layer_run(pre.desc, stream)
+        eb.record(stream)
+        torch.cuda.synchronize()
+        t_chunk.append(ea.elapsed_time(eb))
+    for pre, (c, w, wb) in zip(layers_pre, saved):
+        pre.desc.prefill_chunk, pre.desc.ws, pre.desc.ws_bytes = c, w, wb
+    act["cfg3_prefill_layer_chunk2048"]["prefill_ms_per_stack"] = round(float(np.median(t_chunk[1:])), 3)
+    act["decode_workspace_bytes"] = int(dec_ws.numel())
+    assert fsvd.fsvd_poll_device_error(ws2, stream) == 0
+    del ws2
+
+    # ------------------------------------------------ measured stream bandwidth of this part
+    # The library's read-stream probe (every byte of 4 GiB read once with 16-byte non-temporal
+    # loads) and a torch device copy (1 GiB read + 1 GiB written), beside the 8 TB/s specification.
+    big = torch.empty((2 << 30,), dtype=torch.bfloat16, device=dev).normal_()
+    sink = torch.zeros((64,), dtype=torch.int32, device=dev)
+    nbytes = big.numel() * 2
+    for _ in range(2):
+        fsvd.fsvd_read_stream_probe(big, nbytes, sink, stream)
+    ea.record(stream)
+    for _ in range(5):
+        fsvd.fsvd_read_stream_probe(big, nbytes, sink, stream)
+    eb.record(stream)
+    torch.cuda.synchronize()
+    read_gbs = 5 * nbytes / (ea.elapsed_time(eb) * 1e-3) / 1e9
+    half = big[: big.numel() // 4]
+    dst = torch.empty_like(half)
+    dst.copy_(half)
+    ea.record(stream)
+    for _ in range(5):
+        dst.copy_(half)
+    eb.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * half.numel() * 2 / (ea.elapsed_time(eb) * 1e-3) / 1e9
+    del big, half, dst, sink
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------ the BERT-Base encoder layer (8 x 512, rank 384)
+    from svd_compressed_transformer_amd import configs as CF
+    bert = CF.run_bert_layer(dev, stream)
+    act["cfg1_bert_layer"] = {"allocator_peak": bert["peak_activation_bytes"],
+                              "unfused_count": bert["unfused_activation_bytes"]}
+
     # ------------------------------------------------ report
     M = B * S
     tok_layers = (M + B * ND) * NL
     value = tok_layers / (ms * 1e-3)
     dec_bytes = sum(layer_bytes_decode(cfg, B, S + t + 1, logical) for t in range(ND)) * NL
     dec_gbs = dec_bytes / (t_dec_ms * 1e-3) / 1e9
-    pre_flops = layer_flops_prefill(cfg, M, logical) * NL
-    pre_tflops = pre_flops / (t_pre_ms * 1e-3) / 1e12
-    peak_act = {"prefill_workspace_bytes": int(pre_ws.numel()), "decode_workspace_bytes": int(dec_ws.numel())}
+    proj_flops = layer_flops_prefill(cfg, M, logical) * NL
+    attn_flops = attn_flops_prefill(cfg, B, S) * NL
+    t_proj_ms = t_pre_ms - t_pattn_ms
+    proj_tflops = proj_flops / (t_proj_ms * 1e-3) / 1e12
+    whole_tflops = (proj_flops + attn_flops) / (t_pre_ms * 1e-3) / 1e12
 
     res = {
         "metric": METRIC,
@@ -333,21 +502,34 @@ def main():
                    "layers": NL, "batch": B, "prefill_len": S, "decode_steps": ND, "hidden": cfg.d,
                    "heads": cfg.Hq, "head_dim": cfg.D, "d_ff": cfg.d_ff, "rank": logical["q"], "stored_rank": 1640},
         "prefill": {"ms": round(t_pre_ms, 3), "tokens_per_s_per_layer": round(M * NL / (t_pre_ms * 1e-3), 1),
-                    "proj_tflops": round(pre_tflops, 1), "mfma_frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4)},
+                    "attention_ms": round(t_pattn_ms, 3),
+                    "proj_tflops": round(proj_tflops, 1), "proj_mfma_frac": round(proj_tflops / BF16_PEAK_TFLOPS, 4),
+                    "whole_tflops": round(whole_tflops, 1),
+                    "whole_mfma_frac": round(whole_tflops / BF16_PEAK_TFLOPS, 4),
+                    "note": "proj: projection flops over the prefill time less the live-timed attention (RMSNorm "
+                            "statistics kernels stay in); whole: projection + causal attention flops over the "
+                            "whole prefill time"},
         "decode": {"ms": round(t_dec_ms, 3), "tokens_per_s_per_layer": round(B * ND * NL / (t_dec_ms * 1e-3), 1),
                    "us_per_layer_step": round(t_dec_ms * 1e3 / (ND * NL), 2),
                    "algorithmic_gbs": round(dec_gbs, 1), "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                   "hbm_frac_of_measured_read": round(dec_gbs / read_gbs, 4),
                    "one_graph_per_step": {"ms": round(t_dec_stack_ms, 3),
                                           "us_per_layer_step": round(t_dec_stack_ms * 1e3 / (ND * NL), 2)}},
         "roofline": {"bound": "hbm", "kernel": "attn_decode_split (+combine)", "achieved": round(attn_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(), "avg_us": round(attn_us, 2),
-                     "algorithmic_bytes": int(attn_bytes), "kv_positions": int(L_mid)},
-        "peak_activation_bytes": peak_act,
+                     "algorithmic_bytes": int(attn_bytes), "kv_positions": int(L_mid),
+                     "frac_of_measured_read": round(attn_gbs / read_gbs, 4)},
+        "measured_stream_gbs": {"read": round(read_gbs, 1), "copy": round(copy_gbs, 1),
+                                "note": "fsvd_read_stream_probe over 4 GiB (read) and a 1 GiB torch device copy (read + write)"},
+        "peak_activation_bytes": act,
+        "bert_layer": {"ms": bert["ms_per_layer"], "tokens_per_s_per_layer": bert["tokens_per_s_per_layer"],
+                       "proj_tflops": bert["projections"]["tflops"],
+                       "proj_mfma_frac": bert["projections"]["mfma_frac"]},
     }
     if not args.no_cpu:
         log("cpu oracle baseline ...")
-        res["cpu_baseline"] = cpu_baseline(cfg)
+        res["cpu_baseline"] = cpu_baseline(cfg, M, B * ND)
     for g in graphs:
         fsvd.fsvd_graph_destroy(g)
     print(json.dumps(res))

@@ -220,25 +220,24 @@ fsvd_status_t enqueue_qkv(const QkvDims& q, const void* x, bool norm, const void
     g.A = a_in; g.lda = q.d; g.Bm = (const bf16_t*)A; g.ldb = q.d;
     g.M = M; g.N = rtot; g.K = q.d; g.C = (bf16_t*)wb.z; g.ldc = rtot; g.rstd = rstd; g.err = wb.err;
     TRY(launch_gemm(g, GEPI_STORE, st));
-    // phase 2: one launch per branch (different ranks), RoPE + cache append in the epilogue
+    // phase 2: the three branches (different ranks and output widths) as column segments of one
+    // grouped launch, RoPE + cache append in the epilogue
     const void* Vs[3] = {Vq, Vk, Vv};
     const int rs[3] = {q.rq, q.rk, q.rv};
     const int offs[3] = {0, q.rq, q.rq + q.rk};
     const int Ns[3] = {q.Hq * q.D, q.Hkv * q.D, q.Hkv * q.D};
-    for (int i = 0; i < 3; ++i) {
-        GemmArgs h{};
-        h.A = (const bf16_t*)wb.z; h.lda = rtot; h.a_col_off = offs[i];
-        h.Bm = (const bf16_t*)Vs[i]; h.ldb = rs[i];
-        h.M = M; h.N = Ns[i]; h.K = rs[i];
-        h.S = q.S; h.Hq = q.Hq; h.Hkv = q.Hkv; h.D = q.D; h.rope_theta = q.theta; h.L_max = q.L_max;
-        h.seqlens = seqlens; h.row_off = q.row_off;
-        h.q_out = (bf16_t*)q_out; h.k_cache = (bf16_t*)kc; h.v_cache = (bf16_t*)vc;
-        h.k_out = (bf16_t*)k_out; h.v_out = (bf16_t*)v_out;
-        h.seg = i;
-        h.err = wb.err;
-        TRY(launch_gemm(h, GEPI_QKV, st));
-    }
-    return FSVD_OK;
+    GemmArgs h{};
+    h.A = (const bf16_t*)wb.z; h.lda = rtot;
+    h.nseg = 3;
+    for (int i = 0; i < 3; ++i) h.segs[i] = GemmArgs::Seg{(const bf16_t*)Vs[i], (int64_t)rs[i], rs[i], offs[i], Ns[i]};
+    h.Bm = (const bf16_t*)Vq; h.ldb = q.rq; h.K = std::max(q.rq, std::max(q.rk, q.rv));
+    h.M = M; h.N = Ns[0] + Ns[1] + Ns[2];
+    h.S = q.S; h.Hq = q.Hq; h.Hkv = q.Hkv; h.D = q.D; h.rope_theta = q.theta; h.L_max = q.L_max;
+    h.seqlens = seqlens; h.row_off = q.row_off;
+    h.q_out = (bf16_t*)q_out; h.k_cache = (bf16_t*)kc; h.v_cache = (bf16_t*)vc;
+    h.k_out = (bf16_t*)k_out; h.v_out = (bf16_t*)v_out;
+    h.err = wb.err;
+    return launch_gemm(h, GEPI_QKV, st);
 }
 
 struct MlpDims {
@@ -972,6 +971,12 @@ fsvd_status_t fsvd_layernorm(const void* x, const void* residual, const void* ga
     TRY(opt_ptr(residual, "residual"));
     return launch_layernorm((const bf16_t*)x, (const bf16_t*)residual, (const bf16_t*)gamma, (const bf16_t*)beta, eps, M,
                             d, (bf16_t*)y, (hipStream_t)stream);
+}
+
+fsvd_status_t fsvd_read_stream_probe(const void* src, size_t bytes, void* out, fsvd_stream_t stream) {
+    TRY(need_ptr(src, "src")); TRY(need_ptr(out, "out"));
+    if (bytes < 16) return fail(FSVD_ERR_INVALID_ARG, "bytes must be at least 16");
+    return launch_read_stream(src, bytes, (uint32_t*)out, (hipStream_t)stream);
 }
 
 fsvd_status_t fsvd_seqlens_advance(int32_t* cache_seqlens, int64_t B, int32_t n, fsvd_stream_t stream) {

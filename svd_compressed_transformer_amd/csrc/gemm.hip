@@ -259,9 +259,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
     extern __shared__ u32x4 smem[];
     using T = Tile<BM, BN>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+    // the problem of this workgroup: the launch's, or one column segment of a grouped launch
+    const bf16_t* Bm = g.Bm;
+    int64_t ldb = g.ldb;
+    int K = g.K, N = g.N, acol = g.a_col_off, seg = g.seg;
+    const int tiles_m = (g.M + BM - 1) / BM;
+    int tiles_n = (g.N + BN - 1) / BN;
+    if constexpr (EPI == GEPI_QKV) {
+        if (g.nseg > 1) {
+            tiles_n = 0;
+            for (int s = 0; s < g.nseg; ++s) tiles_n += (g.segs[s].N + BN - 1) / BN;
+        }
+    }
     int tm, tn;
     tile_coords<(BM >= 256 ? 4 : 8)>(tiles_m, tiles_n, &tm, &tn);
+    if constexpr (EPI == GEPI_QKV) {
+        if (g.nseg > 1) {  // segment of column tile tn, and tn within it
+            int s = 0;
+            while (s + 1 < g.nseg && tn >= (g.segs[s].N + BN - 1) / BN) tn -= (g.segs[s++].N + BN - 1) / BN;
+            Bm = g.segs[s].Bm; ldb = g.segs[s].ldb; K = g.segs[s].K; acol = g.segs[s].a_col_off; N = g.segs[s].N;
+            seg = s;
+        }
+    }
     const int m0 = tm * BM, n0 = tn * BN;
     if constexpr (EPI == GEPI_ACC32) {
         if (m0 >= n0 + BN) return;  // wholly below the diagonal of a symmetric product (whole workgroup)
@@ -269,7 +288,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
 
     T t;
     t.zero();
-    t.run(g.A + g.a_col_off, g.lda, g.Bm, g.ldb, m0, n0, g.M, g.N, g.K, smem, tid);
+    t.run(g.A + acol, g.lda, Bm, ldb, m0, n0, g.M, N, K, smem, tid);
     T t2;  // up accumulator (SwiGLU only)
     if constexpr (EPI == GEPI_SWIGLU) {
         t2.zero();
@@ -325,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
         constexpr int LPR = T::WN / 16;    // lanes per row
         constexpr int RP = 64 / LPR;       // rows per pass
         const int halfD = g.D >> 1;
-        const bool rope = g.seg != 2 && g.rope_theta > 0.f;
+        const bool rope = seg != 2 && g.rope_theta > 0.f;
         const int pr0 = (lane % LPR) * 8;             // first pair slot of the lane in the row
         const int h = pr0 / halfD, i0 = pr0 % halfD;  // head within the wave tile, pair index
         const int c1 = h * g.D + i0, c2 = c1 + halfD;  // staged columns of the two halves
@@ -348,16 +367,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
                 const int grow = g.row_off + row;  // token index within the call
                 const int b = grow / g.S, s = grow - b * g.S;
                 pp = (g.seqlens ? (int64_t)g.seqlens[b] : 0) + s;
-                if (g.seg == 0) dr = (int64_t)row * g.N;
-                else if (pp >= 0 && pp < g.L_max) dr = ((int64_t)b * g.L_max + pp) * g.N;
+                if (seg == 0) dr = (int64_t)row * N;
+                else if (pp >= 0 && pp < g.L_max) dr = ((int64_t)b * g.L_max + pp) * N;
                 else set_dev_error(g.err, FSVD_DEVERR_KV_OVERFLOW);
             }
             rpos[r] = pp;
             rdst[r] = dr;
         }
         __syncthreads();
-        bf16_t* dst = g.seg == 0 ? g.q_out : (g.seg == 1 ? g.k_cache : g.v_cache);
-        bf16_t* dbg = g.seg == 1 ? g.k_out : (g.seg == 2 ? g.v_out : nullptr);
+        bf16_t* dst = seg == 0 ? g.q_out : (seg == 1 ? g.k_cache : g.v_cache);
+        bf16_t* dbg = seg == 1 ? g.k_out : (seg == 2 ? g.v_out : nullptr);
 #pragma unroll 1
         for (int i = 0; i < T::FI; ++i) {
             stage(i);
@@ -365,7 +384,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
             for (int pass = 0; pass < 32 / RP; ++pass) {
                 const int r = pass * RP + lane / LPR;
                 const int row = wm + i * 32 + r;
-                if (row >= g.M || wn + c2 >= g.N) continue;
+                if (row >= g.M || wn + c2 >= N) continue;
                 const int tr_ = row - m0;  // row within the tile
                 const int64_t p = rpos[tr_];
                 const int64_t drow = rdst[tr_];
@@ -391,8 +410,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
                     *reinterpret_cast<u32x4*>(dst + drow + wn + c2) = v2;
                 }
                 if (dbg) {
-                    *reinterpret_cast<u32x4*>(dbg + (int64_t)row * g.N + wn + c1) = v1;
-                    *reinterpret_cast<u32x4*>(dbg + (int64_t)row * g.N + wn + c2) = v2;
+                    *reinterpret_cast<u32x4*>(dbg + (int64_t)row * N + wn + c1) = v1;
+                    *reinterpret_cast<u32x4*>(dbg + (int64_t)row * N + wn + c2) = v2;
                 }
             }
         }
@@ -506,9 +525,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
     }
 }
 
+// column tiles of width bn: of the single problem, or summed over the segments of a grouped launch
+int col_tiles(const GemmArgs& g, int bn) {
+    if (g.nseg <= 1) return (g.N + bn - 1) / bn;
+    int t = 0;
+    for (int s = 0; s < g.nseg; ++s) t += (g.segs[s].N + bn - 1) / bn;
+    return t;
+}
+
 template <int BM, int BN, int EPI>
 fsvd_status_t launch_t(const GemmArgs& g, hipStream_t st) {
-    const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+    const int tiles = ((g.M + BM - 1) / BM) * col_tiles(g, BN);
     const size_t lds = Tile<BM, BN>::LDS_BYTES;
     if (const fsvd_status_t s = allow_dynamic_lds((const void*)gemm_kernel<BM, BN, EPI>, lds, "gemm")) return s;
     gemm_kernel<BM, BN, EPI><<<tiles, kThreads, lds, st>>>(g);
@@ -522,7 +549,7 @@ fsvd_status_t launch_t(const GemmArgs& g, hipStream_t st) {
 // D = 128 it needs the 128-wide wave tiles of BN = 256.
 template <int EPI>
 fsvd_status_t launch_epi(const GemmArgs& g, hipStream_t st) {
-    auto tiles = [&](int bm, int bn) { return ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn); };
+    auto tiles = [&](int bm, int bn) { return ((g.M + bm - 1) / bm) * col_tiles(g, bn); };
     if constexpr (EPI == GEPI_ACC32) {
         // square tiles; about half of them (below the diagonal) exit at once
         if (tiles(256, 256) >= 1024) return launch_t<256, 256, EPI>(g, st);
@@ -545,6 +572,11 @@ fsvd_status_t launch_gemm(const GemmArgs& g, int epi, hipStream_t st) {
     if (g.M <= 0 || g.N <= 0) return FSVD_OK;
     if (g.K <= 0 || (epi == GEPI_SWIGLU && g.K2 <= 0)) return fail(FSVD_ERR_INVALID_ARG, "gemm: empty reduction");
     if (epi == GEPI_QKV && (g.D != 64 && g.D != 128)) return fail(FSVD_ERR_UNSUPPORTED, "RoPE epilogue needs D in {64,128}");
+    if (g.nseg > 1) {
+        if (epi != GEPI_QKV || g.nseg > 3) return fail(FSVD_ERR_UNSUPPORTED, "gemm: grouped launches are Q/K/V, 2-3 segments");
+        for (int s = 0; s < g.nseg; ++s)
+            if (g.segs[s].K <= 0 || g.segs[s].N <= 0) return fail(FSVD_ERR_INVALID_ARG, "gemm: empty segment %d", s);
+    }
     switch (epi) {
         case GEPI_STORE: return launch_epi<GEPI_STORE>(g, st);
         case GEPI_LINEAR: return launch_epi<GEPI_LINEAR>(g, st);

@@ -122,7 +122,36 @@ __global__ __launch_bounds__(256) void transpose_kernel(const bf16_t* __restrict
     }
 }
 
+// Read stream: every 16-byte vector of [p, p + n16) read once (non-temporal: the bytes pass
+// through, nothing is kept in the caches), four independent loads per lane in flight per
+// iteration; the XOR of everything read is folded into out[blockIdx.x % 64] so no load is dead.
+__global__ __launch_bounds__(256) void read_stream_kernel(const u32x4* __restrict__ p, int64_t n16, uint32_t* out) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4 a = __builtin_nontemporal_load(p + i), b = __builtin_nontemporal_load(p + i + stride);
+        const u32x4 c = __builtin_nontemporal_load(p + i + 2 * stride), d = __builtin_nontemporal_load(p + i + 3 * stride);
+        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 a = __builtin_nontemporal_load(p + i);
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    for (int off = 32; off > 0; off >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, off);
+    if ((threadIdx.x & 63) == 0) atomicXor(out + (blockIdx.x & 63), acc);
+}
+
 }  // namespace
+
+fsvd_status_t launch_read_stream(const void* src, size_t bytes, uint32_t* out, hipStream_t st) {
+    const int64_t n16 = (int64_t)(bytes / 16);
+    if (n16 <= 0) return FSVD_OK;
+    const int64_t want = (n16 + 255) / 256;
+    const int grid = (int)std::min<int64_t>(want, 256 * 8);  // 8 workgroups per CU
+    read_stream_kernel<<<grid, 256, 0, st>>>((const u32x4*)src, n16, out);
+    return check_launch("read_stream");
+}
 
 fsvd_status_t launch_prepack(void* dst, int64_t ld_dst, int64_t cols_pad, int64_t row0, const void* src, int64_t rows,
                              int64_t cols, int64_t ld_src, int64_t rows_pad, size_t es, const void* col_scale,

@@ -118,6 +118,8 @@ fsvd_status_t launch_prepack(void* dst, int64_t ld_dst, int64_t cols_pad, int64_
 fsvd_status_t launch_layernorm(const bf16_t* x, const bf16_t* res, const bf16_t* g, const bf16_t* b, float eps,
                                int64_t M, int64_t d, bf16_t* y, hipStream_t st);
 fsvd_status_t launch_seqlens_advance(int32_t* sl, int64_t B, int32_t n, hipStream_t st);
+// reads `bytes` (rounded down to 16) once; folds an XOR of them into out[0..63]
+fsvd_status_t launch_read_stream(const void* src, size_t bytes, uint32_t* out, hipStream_t st);
 
 // ---------------------------------------------------------------- prefill (MFMA) GEMM
 enum GemmEpi : int {
@@ -146,6 +148,13 @@ struct GemmArgs {
     const int32_t* seqlens;      // GEPI_QKV: position of row (b, s) = seqlens[b] + s (NULL: s)
     int row_off;                 // GEPI_QKV: row m of this launch is token row_off + m of the call
                                  // ([B, S] flattened: b = (row_off + m) / S); q_out keeps local rows
+    // GEPI_QKV grouped launch: nseg (2 or 3) column segments side by side in one grid, segment s
+    // with its own B operand, rank and A column range (seg s = q, k, v); nseg 0 or 1: the single
+    // problem above (Bm, ldb, K, a_col_off, N, seg)
+    int nseg;
+    struct Seg {
+        const bf16_t* Bm; int64_t ldb; int K; int a_col_off; int N;
+    } segs[3];
     float* C32;                  // GEPI_ACC32: fp32 accumulator [M, ldc]
     bf16_t *q_out, *k_cache, *v_cache, *k_out, *v_out;
     int* err;

@@ -73,6 +73,7 @@ _SIGS = {
     "fsvd_swift_factors": (C.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "fsvd_layernorm": (C.c_int, [_vp, _vp, _vp, _vp, _f32, _i64, _i64, _vp, C.c_int, _vp]),
     "fsvd_seqlens_advance": (C.c_int, [_vp, _i64, _i32, _vp]),
+    "fsvd_read_stream_probe": (C.c_int, [_vp, _sz, _vp, _vp]),
     "fsvd_decoder_layer_ws": (_sz, [C.POINTER(DecoderLayerDesc)]),
     "fsvd_decoder_layer_run": (C.c_int, [C.POINTER(DecoderLayerDesc), _vp]),
     "fsvd_decoder_layer_capture": (C.c_int, [C.POINTER(DecoderLayerDesc), C.POINTER(_vp)]),
@@ -259,6 +260,10 @@ def fsvd_swift_factors(Wt, d_out, d_in, VkT, k, Ut, Vt, ws, ws_bytes, stream=Non
 
 def fsvd_layernorm(x, residual, gamma, beta, eps, M, d, y, dtype, stream=None):
     _check(lib().fsvd_layernorm(_p(x), _p(residual), _p(gamma), _p(beta), eps, M, d, _p(y), dtype, _s(stream)))
+
+
+def fsvd_read_stream_probe(src, nbytes, out, stream=None):
+    _check(lib().fsvd_read_stream_probe(_p(src), nbytes, _p(out), _s(stream)))
 
 
 def fsvd_seqlens_advance(cache_seqlens, B, n, stream=None):
