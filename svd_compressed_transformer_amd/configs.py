@@ -10,6 +10,9 @@ One JSON line per measurement on stdout:
   projection, composed of the entry points (Q/K/V, attention without mask, O + residual,
   LayerNorm, GELU MLP + residual, LayerNorm), eager: layer time, the projections' TFLOP/s and
   fraction of the bf16 MFMA peak, attention time, peak activation bytes.
+- prefill_llama7b_chunks: one Llama-7B-shaped layer, prefill of 4 x 2048 tokens, at pass sizes
+  of 8192 (the default: one pass), 4096, 2048 and 1024 token rows: time per layer, projection
+  TFLOP/s over the layer time, and the workspace each pass size needs.
 - decode_llama7b_b{1,8,16}: 4 distinct Llama-7B-shaped layers (rank 1638 on every projection),
   history held at 2048 (no length advance): per-layer graph replay (the measured configuration),
   one graph per decode step, and eager launches; tokens/s per layer, achieved GB/s of the
@@ -194,6 +197,46 @@ def run_bert_layer(dev, stream):
             "layer_io_bytes": int(io)}
 
 
+# ----------------------------------------------------------------------------- Llama-7B prefill passes
+
+
+def run_prefill_chunks(dev, stream, chunks=(0, 4096, 2048, 1024)):
+    """One Llama-7B-shaped layer (rank 1638, RMSNorm weights folded), prefill of 4 x 2048 tokens,
+    at several pass sizes (prefill_chunk rows; 0 = the default, the whole 8192 rows in one pass):
+    time per layer, projection TFLOP/s (the layer's flops less the causal attention's, over the
+    whole layer time) and the workspace the pass size needs."""
+    cfg, B, S = I.CFG3, I.CFG3_BATCH, I.CFG3_PREFILL
+    M = B * S
+    sl = torch.zeros((1, B), dtype=torch.int32, device=dev)
+    x = torch.randn((B, S, cfg.d), device=dev).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    lay = StackLayer(cfg, dict(cfg.ranks), B, S, S, 11, dev, x, y, sl[0], advance=0)
+    r = lay.logical
+    d, qd, kd = cfg.d, cfg.Hq * cfg.D, cfg.Hkv * cfg.D
+    proj_flops = 2 * M * (r["q"] * (d + qd) + r["k"] * (d + kd) + r["v"] * (d + kd) + r["o"] * (qd + d) +
+                          r["gate"] * (d + cfg.d_ff) + r["up"] * (d + cfg.d_ff) + r["down"] * (cfg.d_ff + d))
+    out = {"config": "prefill_llama7b_chunks", "batch": B, "seq": S, "rank": r["q"], "passes": []}
+    for chunk in chunks:
+        lay.desc.prefill_chunk = chunk
+        ws = fsvd.workspace(fsvd.fsvd_decoder_layer_ws(lay.desc), device=dev)
+        lay.desc.ws, lay.desc.ws_bytes = ws.data_ptr(), ws.numel()
+
+        def layer():
+            fsvd.fsvd_decoder_layer_run(lay.desc, stream)
+
+        ms = timed_median(layer, stream)
+        assert fsvd.fsvd_poll_device_error(ws, stream) == 0
+        out["passes"].append({"chunk_rows": chunk or 8192, "ms_per_layer": round(ms, 4),
+                              "tokens_per_s_per_layer": round(M / (ms * 1e-3), 1),
+                              "proj_tflops_incl_attention_time": round(proj_flops / (ms * 1e-3) / 1e12, 1),
+                              "workspace_bytes": int(ws.numel())})
+        del ws
+        torch.cuda.empty_cache()
+    del lay
+    torch.cuda.empty_cache()
+    return out
+
+
 # ----------------------------------------------------------------------------- decode stacks
 
 
@@ -369,7 +412,8 @@ def main():
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.set_stream(stream)
     runs = [("linear_fp32", lambda: run_linear_fp32(dev, stream)),
-            ("bert_layer", lambda: run_bert_layer(dev, stream))]
+            ("bert_layer", lambda: run_bert_layer(dev, stream)),
+            ("prefill_llama7b_chunks", lambda: run_prefill_chunks(dev, stream))]
     for B in I.CFG2_BATCHES:
         runs.append((f"decode_llama7b_b{B}",
                      lambda B=B: run_decode_stack(f"decode_llama7b_b{B}", I.CFG2, dict(I.CFG2.ranks), B,

@@ -1,0 +1,48 @@
+"""Build and run the measurement probes:
+
+    python -m svd_compressed_transformer_amd.probes [grid_barrier]
+
+grid_barrier: the cost of one grid-wide barrier with one workgroup per CU (see grid_barrier.hip);
+prints one JSON line per (mode, workgroup count).
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+from svd_compressed_transformer_amd import _build
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PROBES = ("grid_barrier",)
+
+
+def binary(name: str) -> str:
+    return os.path.join(_build.BUILD_DIR, f"probe_{name}")
+
+
+def build(name: str) -> str:
+    os.makedirs(_build.BUILD_DIR, exist_ok=True)
+    out = binary(name)
+    cmd = [_build.HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", os.path.join(HERE, f"{name}.hip"), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for probe {name}:\n{r.stderr}")
+    return out
+
+
+def main(argv) -> int:
+    names = argv or list(PROBES)
+    for n in names:
+        if n not in PROBES:
+            raise SystemExit(f"unknown probe {n!r}; known: {PROBES}")
+        exe = binary(n) if os.path.exists(binary(n)) else build(n)
+        r = subprocess.run([exe])
+        if r.returncode != 0:
+            return r.returncode
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
