@@ -2,8 +2,9 @@
  * fsvd.h - C ABI of the fused low-rank transformer-layer library for AMD Instinct MI355X (gfx950).
  *
  * The library implements the serving hot path of an SVD-compressed transformer layer: every
- * dense projection W is replaced by a factor pair and applied as y = (x . U) . V, with the
- * rank-r intermediate kept in on-chip tiles, on packed Q/K/V and O projections and on a packed
+ * dense projection W is replaced by a factor pair and applied as y = (x . U) . V (two fused
+ * kernels per projection: the rank-r intermediate z is accumulated in fp32 on chip and stored once
+ * in bf16 for the second), on packed Q/K/V and O projections and on a packed
  * gate|up SwiGLU MLP (GELU for encoder layers), feeding attention over a contiguous dense KV
  * cache; each layer's decode step can be captured once as a hipGraph and replayed per token.
  *
@@ -197,8 +198,11 @@ fsvd_status_t fsvd_lowrank_qkv(const void* x, int64_t B, int64_t S, int64_t d,
  *   Vt_g NULL; exact erf form);  y = residual + (t . Ut_d^T) . Vt_d^T
  * x [M, d]; A_gu [r_g + r_u, d]; Vt_g, Vt_u [d_ff, r_g|r_u]; Ut_d [r_d, d_ff]; Vt_d [d, r_d];
  * residual [M, d] or NULL (may alias y); y [M, d].  All contiguous.  bf16 only.
- * The d_ff-wide g, u, t never reach HBM on the MFMA path; at decode sizes t passes through
- * the workspace as a B x d_ff vector.
+ * g and u never leave the registers of the gate|up phase-2 kernel: SiLU(g) * u (GELU(u)) is
+ * formed in its epilogue and only t is stored.  t [M, d_ff] and the rank activations z pass
+ * through the workspace between kernels: at decode sizes (M <= 32) a few hundred KB that stay in
+ * L2; at prefill sizes they are written once and read once (the decoder layer bounds them by
+ * running its tokens in passes of at most prefill_chunk rows).
  * ------------------------------------------------------------------------------------------ */
 size_t fsvd_lowrank_mlp_packed_ws(int64_t M, int64_t d, int64_t r_g, int64_t r_u, int64_t d_ff, int64_t r_d);
 fsvd_status_t fsvd_lowrank_mlp_packed(const void* x, int64_t M, int64_t d,
