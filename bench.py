@@ -2,7 +2,7 @@
 
 Workload (one "step"): a stack of distinct Llama-7B-shaped low-rank decoder layers (hidden 4096,
 32 heads x 128, SwiGLU 11008 with packed gate|up factors, every rank 40% -> 1638, stored padded
-to 1640), batch 4: prefill of 2048 tokens per sequence through every layer (bf16 MFMA path,
+to 1664), batch 4: prefill of 2048 tokens per sequence through every layer (bf16 MFMA path,
 dense KV written), then 128 decode steps, each one hipGraph replay per layer.  The stack holds
 several layer copies (weights and KV caches) so the working set far exceeds the 256 MB
 Infinity Cache.  Inputs are seeded synthetic draws (see svd_compressed_transformer_amd.inputs).
@@ -500,7 +500,7 @@ def main():
         "config": {"workload": "llama-7b-shaped low-rank layer stack: prefill 4x2048 then 128 graph-replayed "
                                "decode steps (batch 4)",
                    "layers": NL, "batch": B, "prefill_len": S, "decode_steps": ND, "hidden": cfg.d,
-                   "heads": cfg.Hq, "head_dim": cfg.D, "d_ff": cfg.d_ff, "rank": logical["q"], "stored_rank": 1640},
+                   "heads": cfg.Hq, "head_dim": cfg.D, "d_ff": cfg.d_ff, "rank": logical["q"], "stored_rank": int(layers_pre[0].ranks["r_q"])},
         "prefill": {"ms": round(t_pre_ms, 3), "tokens_per_s_per_layer": round(M * NL / (t_pre_ms * 1e-3), 1),
                     "attention_ms": round(t_pattn_ms, 3),
                     "proj_tflops": round(proj_tflops, 1), "proj_mfma_frac": round(proj_tflops / BF16_PEAK_TFLOPS, 4),

@@ -101,7 +101,9 @@ const char* fsvd_last_error(void);            /* thread-local detail of this thr
  * (row stride ld_dst >= cols_pad): item i occupies rows_pad[i] rows; its first rows[i] rows
  * hold src[i] (columns [0, cols[i]), the rest of the row zero) and the remaining rows are
  * zero.  Used both to stack Ut blocks (A_qkv = [Ut_q; Ut_k; Ut_v], A_gu = [Ut_gate; Ut_up],
- * each rank padded to a multiple of 8) and to zero-pad the rank columns of a Vt.
+ * each rank padded to a multiple of 8, or better 32) and to zero-pad the rank columns of a Vt.
+ * Ranks padded to a multiple of 32 make every factor row and every row of the rank
+ * activations z start on a 64-byte boundary, which the prefill-size products read faster.
  * Bit-exact copy.  items is a HOST array; src pointers are device pointers.
  * ------------------------------------------------------------------------------------------ */
 typedef struct {

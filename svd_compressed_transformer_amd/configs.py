@@ -26,7 +26,7 @@ One JSON line per measurement on stdout:
 - attn_factorized_bert / attn_factorized_llama7b_s2048: attention with Q/K/V rebuilt on chip from
   the rank-r activations (nothing of q, k, v written) against the dense attention over
   materialised q, K, V: BERT-Base encoder (8 x 512, 12 x 64, rank 384, no mask) and a causal
-  Llama-7B prefill of one 2048-token sequence (32 x 128, rank 1640, RoPE); the bytes of q, k, v the
+  Llama-7B prefill of one 2048-token sequence (32 x 128, rank 1638 stored as 1664, RoPE); the bytes of q, k, v the
   factorised form never writes.
 - attn_lowrank_history_llama7b_b{1,4}: the decode attention of a Llama-7B-shaped layer over a
   2048-token history, from the dense KV cache against the layout the dense cache replaces
@@ -294,7 +294,7 @@ def run_decode_stack(name, cfg, ranks, B, history, layers, dev, stream):
 def run_attn_history(B, history, dev, stream, copies=4):
     cfg = I.CFG2
     Hq, Hkv, D = cfg.Hq, cfg.Hkv, cfg.D
-    r = 1640  # rank 1638 stored padded to a multiple of 8
+    r = 1664  # rank 1638 stored padded to a multiple of 32
     L_max = history + 1
     gen = torch.Generator(device=dev)
     gen.manual_seed(5)
@@ -425,7 +425,7 @@ def main():
     runs.append(("attn_factorized_bert", lambda: run_attn_factorized("attn_factorized_bert", 8, 512, 12, 64, 384, 0.0,
                                                                      False, dev, stream)))
     runs.append(("attn_factorized_llama7b_s2048",
-                 lambda: run_attn_factorized("attn_factorized_llama7b_s2048", 1, 2048, 32, 128, 1640, 1e4, True, dev,
+                 lambda: run_attn_factorized("attn_factorized_llama7b_s2048", 1, 2048, 32, 128, 1664, 1e4, True, dev,
                                              stream)))
     for B in (1, 4):
         runs.append((f"attn_lowrank_history_llama7b_b{B}", lambda B=B: run_attn_history(B, 2048, dev, stream)))

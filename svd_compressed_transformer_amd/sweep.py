@@ -3,7 +3,7 @@
     python -m svd_compressed_transformer_amd.sweep [--quick]
 
 Each point builds a stack of distinct Llama-7B-shaped layers (hidden 4096, 32 x 128 heads, SwiGLU
-11008, every projection at rank floor(ratio * 4096) stored padded to a multiple of 8, RMSNorm
+11008, every projection at rank floor(ratio * 4096) stored padded to a multiple of 32, RMSNorm
 weights folded into the packed phase-1 factors) with a dense KV history of random values, then
 times decode steps replayed from per-layer graphs (and from one graph per step) and, for the rank
 sweep, an eager 4 x 2048-token prefill of one layer.  Factors are drawn on the device with the

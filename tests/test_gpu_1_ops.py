@@ -36,9 +36,13 @@ def test_prepack_bit_exact():
     blocks = [I.round_bf16(rng.standard_normal((r, 200))) for r in (13, 8, 1)]
     dev = [to_dev(b) for b in blocks]
     say("prepack rows", [b.shape for b in blocks])
-    packed, rp = pack_rows_dev(dev)
+    packed, rp = pack_rows_dev(dev, pad=8)
     ref, rref = O.pack_rows(blocks, pad_to=8)
     assert rp == rref == [16, 8, 8]
+    assert np.array_equal(bits(packed), I.bf16_bits(ref))
+    packed, rp = pack_rows_dev(dev, pad=32)          # the padding the device helpers use by default
+    ref, rref = O.pack_rows(blocks, pad_to=32)
+    assert rp == rref == [32, 32, 32]
     assert np.array_equal(bits(packed), I.bf16_bits(ref))
     vt = I.round_bf16(rng.standard_normal((37, 13)))
     padded = pad_cols_dev(to_dev(vt), 24)
@@ -61,7 +65,7 @@ def test_prepack_colscale_bit_exact():
     blocks = [I.round_bf16(rng.standard_normal((r, K))) for r in (13, 8)]
     w = I.round_bf16(1.0 + 0.1 * rng.standard_normal(K))
     say("prepack with column scale", [b.shape for b in blocks])
-    packed, rp = pack_rows_dev([to_dev(b) for b in blocks], col_scale=to_dev(w))
+    packed, rp = pack_rows_dev([to_dev(b) for b in blocks], pad=8, col_scale=to_dev(w))
     ref, _ = O.pack_rows(blocks, pad_to=8)
     exp = I.bf16_bits(ref.astype(np.float32) * w.astype(np.float32)[None, :])
     assert rp == [16, 8]
