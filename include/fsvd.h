@@ -200,11 +200,13 @@ fsvd_status_t fsvd_lowrank_qkv(const void* x, int64_t B, int64_t S, int64_t d,
  *   Vt_g NULL; exact erf form);  y = residual + (t . Ut_d^T) . Vt_d^T
  * x [M, d]; A_gu [r_g + r_u, d]; Vt_g, Vt_u [d_ff, r_g|r_u]; Ut_d [r_d, d_ff]; Vt_d [d, r_d];
  * residual [M, d] or NULL (may alias y); y [M, d].  All contiguous.  bf16 only.
- * g and u never leave the registers of the gate|up phase-2 kernel: SiLU(g) * u (GELU(u)) is
- * formed in its epilogue and only t is stored.  t [M, d_ff] and the rank activations z pass
- * through the workspace between kernels: at decode sizes (M <= 32) a few hundred KB that stay in
- * L2; at prefill sizes they are written once and read once (the decoder layer bounds them by
- * running its tokens in passes of at most prefill_chunk rows).
+ * g and u never leave the registers of the kernel that forms them.  At prefill sizes (M > 32)
+ * with equal gate/up and down ranks of 128, 256 or 384 (stored), t does not leave the chip either:
+ * one kernel forms t for 32 columns of d_ff at a time and folds it into z_d = t . Ut_d^T, and
+ * the workspace holds only rank-wide activations (z, per-slice partial sums of z_d, z_d).
+ * Otherwise t [M, d_ff] passes through the workspace between two kernels: at decode sizes
+ * (M <= 32) a few hundred KB that stay in L2; at prefill sizes it is written once and read once
+ * (the decoder layer bounds that by running its tokens in passes of at most prefill_chunk rows).
  * ------------------------------------------------------------------------------------------ */
 size_t fsvd_lowrank_mlp_packed_ws(int64_t M, int64_t d, int64_t r_g, int64_t r_u, int64_t d_ff, int64_t r_d);
 fsvd_status_t fsvd_lowrank_mlp_packed(const void* x, int64_t M, int64_t d,

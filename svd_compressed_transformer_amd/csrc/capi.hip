@@ -247,12 +247,14 @@ struct MlpDims {
 };
 struct MlpBufs {
     void* z_gu;   // [M, rg+ru]
-    void* t;      // [M, d_ff]
+    void* t;      // [M, d_ff] (not used by the fused path)
     void* z_d;    // [M, rd]
     void* xn;     // MFMA path: [M, d]
     float* rstd;  // MFMA path: [M]
     int* err;
     float* part;  // row-dot split-reduction partials, or NULL
+    const MlpFusedPlan* fused;  // MFMA path: t kept on chip (mlp_fused.hip), or NULL
+    void* fpart;  // fused path: per-slice partial z_d (fused->part_bytes)
 };
 
 size_t mlp_scratch(int64_t M, int64_t d, int64_t rgu, int64_t d_ff, int64_t rd) {
@@ -303,6 +305,22 @@ fsvd_status_t enqueue_mlp(const MlpDims& p, const void* x, bool norm, const void
     g.A = a_in; g.lda = p.d; g.Bm = (const bf16_t*)A_gu; g.ldb = p.d;
     g.M = p.M; g.N = rgu; g.K = p.d; g.C = (bf16_t*)wb.z_gu; g.ldc = rgu; g.rstd = rstd; g.err = wb.err;
     TRY(launch_gemm(g, GEPI_STORE, st));
+    if (wb.fused) {
+        // up (gate) phase 2, activation and down phase 1 in one kernel: t stays on chip
+        MlpFusedArgs f{};
+        f.z = (const bf16_t*)wb.z_gu; f.ldz = rgu;
+        f.rg = p.act == FSVD_ACT_SWIGLU ? p.rg : 0; f.ru = p.ru; f.rd = p.rd; f.M = p.M; f.d_ff = p.d_ff;
+        f.Vg = (const bf16_t*)Vg; f.Vu = (const bf16_t*)Vu; f.Ud = (const bf16_t*)Ud; f.ldu = p.d_ff;
+        f.part = (bf16_t*)wb.fpart; f.z_d = (bf16_t*)wb.z_d;
+        TRY(launch_mlp_fused(f, *wb.fused, st));
+        GemmArgs dn{};
+        dn.A = (const bf16_t*)wb.z_d; dn.lda = p.rd; dn.Bm = (const bf16_t*)Vd; dn.ldb = p.rd;
+        dn.M = p.M; dn.N = p.d; dn.K = p.rd; dn.C = (bf16_t*)y; dn.ldc = p.d;
+        dn.residual = (const bf16_t*)residual; dn.ldr = p.d; dn.err = wb.err;
+        TRY(launch_gemm(dn, GEPI_LINEAR, st));
+        if (adv) return launch_seqlens_advance(adv, advB, advn, st);
+        return FSVD_OK;
+    }
     GemmArgs h{};
     h.A = (const bf16_t*)wb.z_gu; h.lda = rgu;
     h.M = p.M; h.N = p.d_ff; h.C = (bf16_t*)wb.t; h.ldc = p.d_ff; h.err = wb.err;
@@ -754,8 +772,20 @@ fsvd_status_t fsvd_lowrank_qkv(const void* x, int64_t B, int64_t S, int64_t d, c
                        (hipStream_t)stream);
 }
 
+// The standalone MLP call at prefill sizes keeps t on chip whenever a fused kernel covers its
+// ranks: its scratch is then z, the per-slice partial z_d and z_d instead of z, t and z_d.
+bool mlp_call_fused(int64_t M, int64_t r_g, int64_t r_u, int64_t d_ff, int64_t r_d, MlpFusedPlan* plan) {
+    return M > kRowdotMaxM && mlp_fused_plan(M, r_g, r_u, d_ff, r_d, plan);
+}
+size_t mlp_call_scratch(int64_t M, int64_t d, int64_t r_g, int64_t r_u, int64_t d_ff, int64_t r_d) {
+    MlpFusedPlan plan{};
+    if (!mlp_call_fused(M, r_g, r_u, d_ff, r_d, &plan)) return mlp_scratch(M, d, r_g + r_u, d_ff, r_d);
+    return align256((size_t)M * (r_g + r_u) * 2) + align256(plan.part_bytes) + align256((size_t)M * r_d * 2) +
+           align256((size_t)M * d * 2) + align256((size_t)M * 4);
+}
+
 size_t fsvd_lowrank_mlp_packed_ws(int64_t M, int64_t d, int64_t r_g, int64_t r_u, int64_t d_ff, int64_t r_d) {
-    return kWsHeader + mlp_scratch(M, d, r_g + r_u, d_ff, r_d);
+    return kWsHeader + mlp_call_scratch(M, d, r_g, r_u, d_ff, r_d);
 }
 
 fsvd_status_t fsvd_lowrank_mlp_packed(const void* x, int64_t M, int64_t d, const void* norm_w, float norm_eps,
@@ -783,8 +813,15 @@ fsvd_status_t fsvd_lowrank_mlp_packed(const void* x, int64_t M, int64_t d, const
     if (ws_bytes < need) return fail(FSVD_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
     Carve c(ws);
     MlpBufs mb{};
+    MlpFusedPlan plan{};
+    const bool fused = mlp_call_fused(M, r_g, r_u, d_ff, r_d, &plan);
     mb.z_gu = c.take((size_t)M * (r_g + r_u) * 2);
-    mb.t = c.take((size_t)M * d_ff * 2);
+    if (fused) {
+        mb.fused = &plan;
+        if (plan.part_bytes) mb.fpart = c.take(plan.part_bytes);
+    } else {
+        mb.t = c.take((size_t)M * d_ff * 2);
+    }
     mb.z_d = c.take((size_t)M * r_d * 2);
     if (M > kRowdotMaxM) {
         mb.xn = c.take((size_t)M * d * 2);

@@ -108,7 +108,23 @@ __device__ __forceinline__ float wave_sum(float v) {
 // ------------------------------------------------------------------ activations
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
-__device__ __forceinline__ float gelu_f(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); }
+// erf by the rational approximation of Abramowitz & Stegun, Handbook of Mathematical Functions,
+// formula 7.1.26 (|error| <= 1.5e-7 in exact arithmetic; about 5e-7 absolute when evaluated in
+// fp32 near 0), branch-free: one hardware reciprocal, one exp2 and five FMAs.  Accurate far
+// beyond the bf16 rounding that follows every GELU here.
+__device__ __forceinline__ float erf_as(float x) {
+    const float ax = fabsf(x);
+    const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
+    float p = fmaf(1.061405429f, t, -1.453152027f);
+    p = fmaf(p, t, 1.421413741f);
+    p = fmaf(p, t, -0.284496736f);
+    p = fmaf(p, t, 0.254829592f);
+    p *= t;
+    const float e = __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);  // e^(-x^2)
+    return copysignf(fmaf(-p, e, 1.0f), x);
+}
+// GELU in its erf form: u/2 * (1 + erf(u / sqrt 2))
+__device__ __forceinline__ float gelu_f(float u) { return 0.5f * u * (1.0f + erf_as(u * 0.70710678118654752f)); }
 
 // RoPE angle for pair i at position p: p * base^i with base = theta^(-2/D) (computed once on the
 // host in double).  base^i by binary exponentiation in double (i < 64: at most 12 products, a few

@@ -160,6 +160,24 @@ struct GemmArgs {
     int* err;
 };
 fsvd_status_t launch_gemm(const GemmArgs& g, int epi, hipStream_t st);
+// ---------------------------------------------------------------- fused MLP middle (prefill)
+// z_d = act(z_u . Vt_u^T [, z_g . Vt_g^T]) . Ut_d^T with t kept on chip (mlp_fused.hip)
+struct MlpFusedArgs {
+    const bf16_t* z; int64_t ldz;     // [M, ldz]: z_g = columns [0, rg), z_u = [rg, rg + ru)
+    int rg, ru, rd, M, d_ff;          // rg = 0: GELU(u); else SiLU(g) * u
+    const bf16_t *Vg, *Vu;            // [d_ff, rg], [d_ff, ru]
+    const bf16_t* Ud; int64_t ldu;    // [rd, ldu]
+    bf16_t* part;                     // [S, M, rd] per-slice partial sums (plan.part_bytes; S > 1 only)
+    bf16_t* z_d;                      // [M, rd]
+};
+struct MlpFusedPlan {
+    int bm, nw, nb, S, cps;           // rows and waves per workgroup, row blocks, d_ff slices, chunks per slice
+    size_t part_bytes;
+};
+// false when no fused kernel covers these ranks (the two-product path is used instead)
+bool mlp_fused_plan(int64_t M, int64_t rg, int64_t ru, int64_t d_ff, int64_t rd, MlpFusedPlan* p);
+fsvd_status_t launch_mlp_fused(const MlpFusedArgs& a, const MlpFusedPlan& p, hipStream_t st);
+
 // out[c, r] = in[r, c] for r < rows, c < cols (bf16, through 64 x 64 LDS tiles)
 fsvd_status_t launch_transpose(const bf16_t* in, int64_t rows, int64_t cols, int64_t ld_in, bf16_t* out,
                                int64_t ld_out, hipStream_t st);

@@ -55,6 +55,26 @@ def test_workspace_queries(L):
     assert fsvd.fsvd_decoder_layer_ws(d) > 256
 
 
+def test_mlp_workspace_keeps_t_on_chip(L):
+    """At prefill sizes the packed MLP keeps t [M, d_ff] on chip when a fused kernel covers its
+    ranks (equal up and down ranks of 128, 256 or 384): the workspace holds z, the per-slice
+    partial z_d (BERT-Base, 4096 rows: 32 blocks of 128 rows x 8 slices of d_ff) and z_d; with
+    ranks no fused kernel covers it holds t instead, and so does every decode-size call."""
+    al = lambda n: (n + 255) // 256 * 256
+    M, d, dff = 4096, 768, 3072
+    common = al(M * d * 2) + al(M * 4)  # normalised input and its per-row rstd (MFMA path)
+    r = 384
+    assert fsvd.fsvd_lowrank_mlp_packed_ws(M, d, 0, r, dff, r) == 256 + al(M * r * 2) + al(8 * M * r * 2) + al(M * r * 2) + common
+    r = 392
+    assert fsvd.fsvd_lowrank_mlp_packed_ws(M, d, 0, r, dff, r) == 256 + al(M * r * 2) + al(M * dff * 2) + al(M * r * 2) + common
+    # one slice when the row blocks alone fill the chip: z_d written directly, no partials
+    M = 16600
+    common = al(M * 256 * 2) + al(M * 4)
+    assert fsvd.fsvd_lowrank_mlp_packed_ws(M, 256, 0, 128, 264, 128) == 256 + 2 * al(M * 128 * 2) + common
+    # decode sizes keep the two-kernel path (t of a few rows stays in L2)
+    assert fsvd.fsvd_lowrank_mlp_packed_ws(16, d, 0, 384, dff, 384) >= 256 + al(16 * dff * 2)
+
+
 def _status(f):
     try:
         f()

@@ -109,6 +109,48 @@ def test_mlp_prefill_swiglu(M):
     assert rel(from_dev(y), ref) <= BF16_TOL
 
 
+# The MLP middle with t kept on chip (one kernel from z_g, z_u to z_d) covers equal gate, up and
+# down ranks of 128, 256, 384 or 512: ragged row blocks and d_ff chunks, many d_ff slices, one
+# slice (z_d written directly), both row-set widths and both pipeline depths.
+@pytest.mark.parametrize("act,r,d,d_ff,M", [
+    ("gelu", 128, 256, 1000, 777),
+    ("gelu", 256, 512, 640, 1500),
+    ("gelu", 384, 768, 3072, 4096),
+    ("gelu", 512, 640, 2048, 300),
+    ("gelu", 128, 256, 264, 16600),
+    ("swiglu", 128, 256, 520, 200),
+    ("swiglu", 256, 512, 1024, 1500),
+])
+def test_mlp_fused_prefill(act, r, d, d_ff, M):
+    say("mlp fused prefill", act, r, d, d_ff, M)
+    rng = np.random.default_rng(r + M)
+    rb = I.round_bf16
+    x = rb(rng.standard_normal((M, d)))
+    res = rb(rng.standard_normal((M, d)))
+    Uu, Vu = map(rb, I.factor_pair(rng, d, d_ff, r))
+    Udn, Vdn = map(rb, I.factor_pair(rng, d_ff, d, r))
+    if act == "swiglu":
+        Ug, Vg = map(rb, I.factor_pair(rng, d, d_ff, r))
+        nw = rb(1.0 + 0.1 * rng.standard_normal(d))
+        A, rg, fact = np.concatenate([Ug, Uu]), r, fsvd.FSVD_ACT_SWIGLU
+    else:
+        Ug = Vg = nw = None
+        A, rg, fact = Uu, 0, fsvd.FSVD_ACT_GELU
+    xd = to_dev(x)
+    y = torch.empty_like(xd)
+    nb = fsvd.fsvd_lowrank_mlp_packed_ws(M, d, rg, r, d_ff, r)
+    ws = fsvd.workspace(nb)
+    fsvd.fsvd_lowrank_mlp_packed(xd, M, d, to_dev(nw) if nw is not None else None, 1e-6, fact, to_dev(A), rg, r,
+                                 to_dev(Vg) if Vg is not None else None, to_dev(Vu), d_ff, to_dev(Udn), to_dev(Vdn), r,
+                                 to_dev(res), y, fsvd.FSVD_BF16, ws, nb)
+    torch.cuda.synchronize()
+    assert fsvd.fsvd_poll_device_error(ws) == 0
+    ref = O.mlp(x, nw, 1e-6, act, Ug, Vg, Uu, Vu, Udn, Vdn, residual=res)
+    err = rel(from_dev(y), ref)
+    say("  err", err)
+    assert err <= BF16_TOL
+
+
 @pytest.mark.parametrize("fold", [False, True])
 def test_decoder_prefill_layer(fold):
     cfg = SMALL
