@@ -60,6 +60,78 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const bf16_t* x, const b
         y[row * d + i] = f2bf((buf[i] - mean) * rstd * bf2f(g[i]) + bf2f(bta[i]));
 }
 
+// The same LayerNorm with one wave per row (4 rows per workgroup) when d is a multiple of 8 and the
+// operands are 16-byte aligned: 16-byte loads and stores, the row (x + res in fp32) held in
+// registers, NV 16-byte vectors per lane at most (d <= 512 * NV).  Statistics in two passes over
+// the registers, reduced across the wave with DPP and lane reads.
+template <int NV>
+__global__ __launch_bounds__(256) void layernorm_wave_kernel(const bf16_t* x, const bf16_t* res, const bf16_t* g,
+                                                             const bf16_t* bta, float eps, int64_t M, int64_t d,
+                                                             bf16_t* y) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;  // whole wave
+    const int lane = threadIdx.x & 63;
+    const int nv = (int)(d / 8);
+    const u32x4* xr = reinterpret_cast<const u32x4*>(x + row * d);
+    const u32x4* rr = res ? reinterpret_cast<const u32x4*>(res + row * d) : nullptr;
+    float v[NV][8];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c = lane + 64 * i;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
+        if (c < nv) {
+            const u32x4 a = xr[c];
+            const uint32_t ea[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[i][2 * e] = bf_lo(ea[e]);
+                v[i][2 * e + 1] = bf_hi(ea[e]);
+            }
+            if (rr) {
+                const u32x4 b = rr[c];
+                const uint32_t eb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[i][2 * e] += bf_lo(eb[e]);
+                    v[i][2 * e + 1] += bf_hi(eb[e]);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s += v[i][e];
+        }
+    }
+    const float mean = wave_sum(s) / (float)d;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+        if (lane + 64 * i < nv)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float dv = v[i][e] - mean;
+                q += dv * dv;
+            }
+    const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)d + eps);
+    const u32x4* gv = reinterpret_cast<const u32x4*>(g);
+    const u32x4* bv = reinterpret_cast<const u32x4*>(bta);
+    u32x4* yr = reinterpret_cast<u32x4*>(y + row * d);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nv) {
+            const u32x4 gg = gv[c], bb = bv[c];
+            const uint32_t eg[4] = {gg.x, gg.y, gg.z, gg.w}, eb[4] = {bb.x, bb.y, bb.z, bb.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[e] = pack_bf2((v[i][2 * e] - mean) * rstd * bf_lo(eg[e]) + bf_lo(eb[e]),
+                                (v[i][2 * e + 1] - mean) * rstd * bf_hi(eg[e]) + bf_hi(eb[e]));
+            yr[c] = u32x4{o[0], o[1], o[2], o[3]};
+        }
+    }
+}
+
 __global__ void seqlens_advance_kernel(int32_t* sl, int64_t B, int32_t n) {
     const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (i < B) sl[i] += n;
@@ -171,6 +243,16 @@ fsvd_status_t launch_prepack(void* dst, int64_t ld_dst, int64_t cols_pad, int64_
 fsvd_status_t launch_layernorm(const bf16_t* x, const bf16_t* res, const bf16_t* g, const bf16_t* b, float eps,
                                int64_t M, int64_t d, bf16_t* y, hipStream_t st) {
     if (M == 0) return FSVD_OK;
+    const bool vec = d % 8 == 0 && d <= 512 * 16 && aligned16(x) && (!res || aligned16(res)) && aligned16(g) &&
+                     aligned16(b) && aligned16(y);
+    if (vec) {
+        const unsigned grid = (unsigned)((M + 3) / 4);
+        if (d <= 512 * 2) layernorm_wave_kernel<2><<<grid, 256, 0, st>>>(x, res, g, b, eps, M, d, y);
+        else if (d <= 512 * 4) layernorm_wave_kernel<4><<<grid, 256, 0, st>>>(x, res, g, b, eps, M, d, y);
+        else if (d <= 512 * 8) layernorm_wave_kernel<8><<<grid, 256, 0, st>>>(x, res, g, b, eps, M, d, y);
+        else layernorm_wave_kernel<16><<<grid, 256, 0, st>>>(x, res, g, b, eps, M, d, y);
+        return check_launch("layernorm");
+    }
     layernorm_kernel<<<(unsigned)M, 256, d * sizeof(float), st>>>(x, res, g, b, eps, d, y);
     return check_launch("layernorm");
 }

@@ -404,16 +404,21 @@ def test_attention_lowrank_history(B, Sq, Hq, Hkv, D, r_k, r_v, L_max, seqlens, 
 # ----------------------------------------------------------------------------- LayerNorm glue (a7)
 
 
-def test_layernorm_residual():
-    rng = np.random.default_rng(3)
-    M, d = 9, 768
+# widths the one-wave-per-row kernel takes (multiples of 8 up to 8192: 768, 4096, 8192, ragged row
+# counts) and those it leaves to the workgroup-per-row kernel (1000, 8200); with and without the
+# residual, and in place (y = x)
+@pytest.mark.parametrize("M,d,with_res,inplace", [(9, 768, True, False), (4097, 768, True, True), (30, 4096, False, False),
+                                                  (7, 8192, True, False), (5, 1000, True, False), (3, 8200, False, True)])
+def test_layernorm_residual(M, d, with_res, inplace):
+    rng = np.random.default_rng(d + M)
     x = I.round_bf16(3 + rng.standard_normal((M, d)))
-    r = I.round_bf16(rng.standard_normal((M, d)))
+    r = I.round_bf16(rng.standard_normal((M, d))) if with_res else None
     g = I.round_bf16(1 + 0.1 * rng.standard_normal(d))
     b = I.round_bf16(0.1 * rng.standard_normal(d))
     xd = to_dev(x)
-    y = torch.empty_like(xd)
-    say("layernorm")
-    fsvd.fsvd_layernorm(xd, to_dev(r), to_dev(g), to_dev(b), 1e-12, M, d, y, fsvd.FSVD_BF16)
+    y = xd if inplace else torch.empty_like(xd)
+    say("layernorm", M, d, with_res, inplace)
+    fsvd.fsvd_layernorm(xd, to_dev(r) if with_res else None, to_dev(g), to_dev(b), 1e-12, M, d, y, fsvd.FSVD_BF16)
     torch.cuda.synchronize()
-    assert rel(from_dev(y), O.layernorm(x + r.astype(np.float64), g, b, 1e-12)) <= BF16_TOL
+    ref = O.layernorm(x + (r.astype(np.float64) if with_res else 0.0), g, b, 1e-12)
+    assert rel(from_dev(y), ref) <= BF16_TOL
