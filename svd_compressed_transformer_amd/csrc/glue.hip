@@ -74,6 +74,9 @@ __global__ __launch_bounds__(256) void layernorm_wave_kernel(const bf16_t* x, co
     const int nv = (int)(d / 8);
     const u32x4* xr = reinterpret_cast<const u32x4*>(x + row * d);
     const u32x4* rr = res ? reinterpret_cast<const u32x4*>(res + row * d) : nullptr;
+    const u32x4* gv = reinterpret_cast<const u32x4*>(g);
+    const u32x4* bv = reinterpret_cast<const u32x4*>(bta);
+    u32x4 gg[NV], bb[NV];  // loaded with the row: one round trip to memory less before the stores
     float v[NV][8];
     float s = 0.f;
 #pragma unroll
@@ -82,6 +85,8 @@ __global__ __launch_bounds__(256) void layernorm_wave_kernel(const bf16_t* x, co
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
         if (c < nv) {
+            gg[i] = gv[c];
+            bb[i] = bv[c];
             const u32x4 a = xr[c];
             const uint32_t ea[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
@@ -113,15 +118,12 @@ __global__ __launch_bounds__(256) void layernorm_wave_kernel(const bf16_t* x, co
                 q += dv * dv;
             }
     const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)d + eps);
-    const u32x4* gv = reinterpret_cast<const u32x4*>(g);
-    const u32x4* bv = reinterpret_cast<const u32x4*>(bta);
     u32x4* yr = reinterpret_cast<u32x4*>(y + row * d);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int c = lane + 64 * i;
         if (c < nv) {
-            const u32x4 gg = gv[c], bb = bv[c];
-            const uint32_t eg[4] = {gg.x, gg.y, gg.z, gg.w}, eb[4] = {bb.x, bb.y, bb.z, bb.w};
+            const uint32_t eg[4] = {gg[i].x, gg[i].y, gg[i].z, gg[i].w}, eb[4] = {bb[i].x, bb[i].y, bb[i].z, bb[i].w};
             uint32_t o[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
