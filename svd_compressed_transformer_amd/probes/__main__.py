@@ -1,9 +1,12 @@
 """Build and run the measurement probes:
 
-    python -m svd_compressed_transformer_amd.probes [grid_barrier]
+    python -m svd_compressed_transformer_amd.probes [grid_barrier] [phase_boundary]
 
 grid_barrier: the cost of one grid-wide barrier with one workgroup per CU (see grid_barrier.hip);
 prints one JSON line per (mode, workgroup count).
+phase_boundary: a decode layer-step modelled as 10 dependent streaming phases, as 10 kernels in a
+graph against one persistent kernel with grid barriers, with and without prefetching the next
+phase's first loads before each barrier (see phase_boundary.hip); one JSON line per variant.
 """
 from __future__ import annotations
 
@@ -14,7 +17,7 @@ import sys
 from svd_compressed_transformer_amd import _build
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-PROBES = ("grid_barrier",)
+PROBES = ("grid_barrier", "phase_boundary")
 
 
 def binary(name: str) -> str:
