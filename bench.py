@@ -136,8 +136,8 @@ def _median_rate(fn, runs=3):
 
 def cpu_baseline(cfg, prefill_tokens_per_layer, decode_tokens_per_layer):
     """The fp64 oracle, as it stands, on bounded samples of the benchmark's own units, on this
-    host's cores: the prefill of one 256-token sequence through one full-size layer (tokens/s per
-    layer) and batch-4 decode layer-steps over a 2048-token history (tokens/s per layer), each the
+    host's cores: the prefill of one 512-token sequence through one full-size layer (tokens/s per
+    layer) and 10 batch-4 decode layer-steps over a 2048-token history (tokens/s per layer), each the
     median of 3 runs; plus single-thread figures for the fp32 linear (x 16 x 256, rank 64) and one
     batch-1 decode layer-step.  ``value`` is the step's mix of prefill and decode tokens (the GPU
     line's unit) at those two rates."""
@@ -145,7 +145,7 @@ def cpu_baseline(cfg, prefill_tokens_per_layer, decode_tokens_per_layer):
     from svd_compressed_transformer_amd import inputs as I
     threads, blas = _blas_threads()
     t_all = time.perf_counter()
-    S_pre = 256
+    S_pre = 512
     p = I.make_decoder_layer(cfg, B=1, S=S_pre, seed=100)
     z = np.zeros((1, S_pre, cfg.Hkv, cfg.D))
 
@@ -156,9 +156,10 @@ def cpu_baseline(cfg, prefill_tokens_per_layer, decode_tokens_per_layer):
 
     r_pre = _median_rate(prefill)
     B, L = 4, 2048
-    kc, vc = I.make_kv_history(B, L + 8, cfg.Hkv, cfg.D, L, seed=101)
+    n_dec = 10  # decode steps per run: with the prefill, about 10-15 s of CPU work in all
+    kc, vc = I.make_kv_history(B, L + n_dec, cfg.Hkv, cfg.D, L, seed=101)
     rng = np.random.default_rng(102)
-    xs = [I.round_bf16(rng.standard_normal((B, 1, cfg.d))) for _ in range(4)]
+    xs = [I.round_bf16(rng.standard_normal((B, 1, cfg.d))) for _ in range(n_dec)]
 
     def decode():
         sl = np.full(B, L)
@@ -199,7 +200,7 @@ def cpu_baseline(cfg, prefill_tokens_per_layer, decode_tokens_per_layer):
             "blas": blas,
             "prefill_tokens_per_s_per_layer": round(r_pre, 2), "decode_tokens_per_s_per_layer": round(r_dec, 3),
             "single_thread": single,
-            "sample": f"numpy fp64 oracle, one full-size layer: prefill of 1 x {S_pre} tokens and 4 decode "
+            "sample": f"numpy fp64 oracle, one full-size layer: prefill of 1 x {S_pre} tokens and {n_dec} decode "
                       f"steps at batch 4 over history {L}, median of 3 runs each; value = the benchmark step's "
                       f"mix ({prefill_tokens_per_layer} prefill + {decode_tokens_per_layer} decode tokens per layer) "
                       f"at those rates; {time.perf_counter() - t_all:.1f} s of CPU work"}
