@@ -46,8 +46,10 @@
  *     never allocates device memory inside these calls and never synchronises, except where a
  *     call says so (capture, poll).
  *   - Workspace: each call that needs scratch takes (ws, ws_bytes); the matching *_ws() query
- *     returns the size.  The first 256 bytes of every workspace are a header whose first int32
- *     is the DEVICE ERROR WORD; a workspace must be zero-filled once before its first use.
+ *     returns the size.  The first 4096 bytes of every workspace are a header: its first int32
+ *     is the DEVICE ERROR WORD, and from byte 64 on it holds the decode attention's partition
+ *     counters, which every call leaves at zero.  A workspace must be zero-filled once before
+ *     its first use; after that the header stays valid whichever calls share the workspace.
  *   - Errors: every call returns fsvd_status_t.  Arguments are validated before any launch
  *     (null pointers, non-positive sizes, misalignment, too-small workspace, unsupported
  *     combinations); on failure nothing is launched and fsvd_last_error() explains.  Launch
@@ -70,7 +72,7 @@ extern "C" {
 
 typedef struct ihipStream_t* fsvd_stream_t; /* a hipStream_t */
 
-#define FSVD_ABI_VERSION 6
+#define FSVD_ABI_VERSION 7
 
 typedef enum {
     FSVD_OK = 0,
@@ -225,8 +227,10 @@ fsvd_status_t fsvd_lowrank_mlp_packed(const void* x, int64_t M, int64_t d,
  * BEFORE this call's Sq tokens were appended (they must already be in the cache).
  * softmax_scale 0 -> 1/sqrt(D).  Sq == 1 uses split-length partitions merged by log-sum-exp
  * (the partition count is fixed by the workspace; lengths are read on the device, so a
- * captured graph stays valid as the cache grows).  Sq > 1 is the correctness path used by
- * prefill and encoder layers.  D must be 64 or 128; Hq % Hkv == 0.  bf16 only.
+ * captured graph stays valid as the cache grows).  The last partition of each (sequence, kv
+ * head) to finish does the merge, counted in the workspace header when B * Hkv <= 1008; beyond
+ * that a second kernel merges.  Sq > 1 (prefill and encoder layers) runs on the matrix cores.
+ * D must be 64 or 128; Hq % Hkv == 0.  bf16 only.
  * n > L_max is clamped to L_max and sets FSVD_DEVERR_SEQ_OVERFLOW.
  * ------------------------------------------------------------------------------------------ */
 size_t fsvd_decode_attn_dense_kv_ws(int64_t B, int64_t Sq, int64_t Hq, int64_t Hkv, int64_t D, int64_t L_max);

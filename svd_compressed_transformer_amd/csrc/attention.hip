@@ -9,8 +9,10 @@
 // partition); its 16 lane groups of 16 lanes each take one position at a time (16 lanes x 8
 // bf16 = one 128-wide head vector), reduce q.k across the lane group with DPP, and keep an
 // online softmax per query head of the GQA group, so a K/V line is read once for all heads
-// that share it.  Partitions are merged by log-sum-exp in a second small kernel.  The length
-// is read on the device from cache_seqlens, so a captured graph stays valid as the cache grows.
+// that share it.  Partitions are merged by log-sum-exp: the last partition of each (sequence, kv
+// head) to finish merges them (a counter per pair in the workspace header), or, without counters,
+// a second small kernel does.  The length is read on the device from cache_seqlens, so a captured
+// graph stays valid as the cache grows.
 //
 // Sq > 1 (prefill and encoder layers) runs on the matrix cores (attention_prefill.hip).
 #include "kernels.h"
@@ -22,7 +24,12 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
 #ifndef FSVD_ATTN_WGS
-#define FSVD_ATTN_WGS 4096  // decode: target workgroups (sequence x kv head x length partition)
+// decode: target workgroups (sequence x kv head x length partition).  Few long partitions beat
+// many short ones: each workgroup ends with its partial stores' round trip and the count, so
+// workgroups that fit the CUs in one round stream best (measured on MI355X, batch 4, 32 heads
+// of 128, 2112 positions, last-partition merge: 512 -> 27.8 us, 1024 -> 30.4 us, 2048 -> 32.4 us,
+// 4096 -> 37.6 us; with the merge in a second kernel, 1024 -> 33.1 us and 4096 -> 34.4 us).
+#define FSVD_ATTN_WGS 512
 #endif
 #ifndef FSVD_ATTN_NP
 #define FSVD_ATTN_NP 2      // decode: positions per lane group per iteration (16 * NP per workgroup)
@@ -32,6 +39,12 @@ constexpr float kNegBig = -1.0e30f;
 #endif
 #ifndef FSVD_ATTN_MERGE_C
 #define FSVD_ATTN_MERGE_C 32  // partition merge: partitions loaded per round trip
+#endif
+#ifndef FSVD_ATTN_LAST_MERGE_C
+#define FSVD_ATTN_LAST_MERGE_C 16 // the same inside the split kernel, whose registers it shares
+#endif
+#ifndef FSVD_ATTN_FUSED_MERGE
+#define FSVD_ATTN_FUSED_MERGE 1  // 0: always merge in the second kernel (for comparisons)
 #endif
 
 // EPL: head elements per lane (D / 16): 8 for D = 128, 4 for D = 64.  G: query heads per kv head.
@@ -51,6 +64,47 @@ __device__ __forceinline__ KV<EPL> ld_kv(const bf16_t* p) {
         r.w[0] = v.x; r.w[1] = v.y;
     }
     return r;
+}
+
+// Log-sum-exp merge of the ns partitions of one (b, h) at head element dd.  part points at the
+// rows of (b, h): [ns][D + 2], the partition's D outputs, then its running max and sum.  Every
+// thread loads its element of C partitions together with their statistics, so the merge costs
+// one round trip to the cache per C partitions.  COHERENT: the rows were written in the same
+// kernel by workgroups on any XCD, so they are read with agent-scope loads (which fetch from the
+// coherent level, not from a line this XCD's L2 may hold).
+template <bool COHERENT, int C>
+__device__ __forceinline__ float merge_partitions(const float* part, int ns, int D, int dd) {
+    auto ld = [](const float* p) {
+        if constexpr (COHERENT) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else return *p;
+    };
+    float M = kNegBig, L = 0.f, O = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += C) {
+        float ms[C], ls[C], os[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const bool ok = s0 + c < ns;
+            const float* row = part + (int64_t)(ok ? s0 + c : s0) * (D + 2);
+            const float mv = ld(row + D);
+            ms[c] = ok ? mv : kNegBig;
+            ls[c] = ld(row + D + 1);
+            os[c] = ld(row + dd);
+        }
+        float mc = M;
+#pragma unroll
+        for (int c = 0; c < C; ++c) mc = fmaxf(mc, ms[c]);
+        const float r = exp2f(M - mc);
+        L *= r;
+        O *= r;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const float w = exp2f(ms[c] - mc);  // 0 for the padding entries (max = -1e30)
+            L += w * ls[c];
+            O += w * os[c];
+        }
+        M = mc;
+    }
+    return O / L;  // L > 0: the partition holding position n - 1 is never empty
 }
 
 // One workgroup = (b, kv head, length partition); 256 threads = 16 lane groups.
@@ -186,54 +240,51 @@ __global__ __launch_bounds__(256) void attn_decode_split(const AttnArgs a) {
         }
         const int h = kvh * G + g;
         float* part = a.part + (((int64_t)b * a.Hq + h) * a.nsplit + split) * (D + 2);
-        part[dd] = O;
+        // agent-scope stores: written through to the level every XCD reads coherently
+        __hip_atomic_store(part + dd, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (dd == 0) {
-            part[D] = M;
-            part[D + 1] = L;
+            __hip_atomic_store(part + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(part + D + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+    }
+    if (a.cnt == nullptr) return;  // attn_decode_combine merges
+
+    // The last partition of (b, kv head) to finish merges all of them.  Every thread waits until
+    // its partial stores have completed before the barrier, and only then is the partition
+    // counted, so the workgroup that takes the last count reads every partition's rows back with
+    // agent-scope loads.  Nothing waits on another workgroup: the others simply exit.  The
+    // counter is reset for the next call.
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+    __syncthreads();
+    __shared__ int is_last;
+    if (tid == 0) {
+        const unsigned old = __hip_atomic_fetch_add(a.cnt + bg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = old + 1 == (unsigned)a.nsplit;
+        if (last) __hip_atomic_store(a.cnt + bg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        is_last = last;
+    }
+    __syncthreads();
+    if (!is_last) return;
+    for (int idx = tid; idx < G * D; idx += 256) {
+        const int g = idx / D, dd = idx - g * D;
+        const int64_t bh = (int64_t)b * a.Hq + kvh * G + g;
+        a.out[bh * D + dd] = f2bf(merge_partitions<true, FSVD_ATTN_LAST_MERGE_C>(a.part + bh * a.nsplit * (D + 2), a.nsplit, D, dd));
     }
 }
 
-// merge partitions: one workgroup per (b, h), one thread per head element.  Every thread loads
-// its element of all partitions together with the partitions' (max, sum) statistics, so the
-// merge costs a single round trip to L2; partitions are taken 16 at a time.
+// merge partitions in a second kernel: one workgroup per (b, h), one thread per head element
 __global__ __launch_bounds__(128) void attn_decode_combine(const AttnArgs a) {
     const int D = a.D, ns = a.nsplit;
     const int bh = blockIdx.x;
     const int t = threadIdx.x;
     if (t >= D) return;
-    const float* part = a.part + (int64_t)bh * ns * (D + 2);
-    constexpr int C = FSVD_ATTN_MERGE_C;
-    float M = kNegBig, L = 0.f, O = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += C) {
-        float ms[C], ls[C], os[C];
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-            const bool ok = s0 + c < ns;
-            const float* row = part + (int64_t)(ok ? s0 + c : s0) * (D + 2);
-            ms[c] = ok ? row[D] : kNegBig;
-            ls[c] = row[D + 1];
-            os[c] = row[t];
-        }
-        float mc = M;
-#pragma unroll
-        for (int c = 0; c < C; ++c) mc = fmaxf(mc, ms[c]);
-        const float r = exp2f(M - mc);
-        L *= r;
-        O *= r;
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-            const float w = exp2f(ms[c] - mc);  // 0 for the padding entries (max = -1e30)
-            L += w * ls[c];
-            O += w * os[c];
-        }
-        M = mc;
-    }
-    a.out[(int64_t)bh * D + t] = f2bf(O / L);
+    a.out[(int64_t)bh * D + t] = f2bf(merge_partitions<false, FSVD_ATTN_MERGE_C>(a.part + (int64_t)bh * ns * (D + 2), ns, D, t));
 }
 
 template <int EPL>
-fsvd_status_t launch_decode_d(const AttnArgs& a, hipStream_t st) {
+fsvd_status_t launch_decode_d(const AttnArgs& args, hipStream_t st) {
+    AttnArgs a = args;
+    if (!FSVD_ATTN_FUSED_MERGE) a.cnt = nullptr;
     const int G = a.Hq / a.Hkv;
     const int grid = a.B * a.Hkv * a.nsplit;
     switch (G) {
@@ -244,7 +295,7 @@ fsvd_status_t launch_decode_d(const AttnArgs& a, hipStream_t st) {
         default: return fail(FSVD_ERR_UNSUPPORTED, "GQA group size %d not in {1,2,4,8}", G);
     }
     fsvd_status_t s = check_launch("attn_decode_split");
-    if (s != FSVD_OK) return s;
+    if (s != FSVD_OK || a.cnt) return s;
     attn_decode_combine<<<a.B * a.Hq, 128, 0, st>>>(a);
     return check_launch("attn_decode_combine");
 }

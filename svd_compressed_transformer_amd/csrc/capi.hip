@@ -337,14 +337,17 @@ fsvd_status_t enqueue_mlp(const MlpDims& p, const void* x, bool norm, const void
                           FSVD_BF16, lb, adv, advB, advn, st);
 }
 
+// ws: the workspace (its header holds the device error word and the decode partition counters)
 fsvd_status_t enqueue_attn(const void* q, const void* kc, const void* vc, int64_t L_max, const int32_t* seqlens, int B,
                            int Sq, int Hq, int Hkv, int D, float scale, int causal, void* out, float* part, int nsplit,
-                           int* err, hipStream_t st) {
+                           void* ws, hipStream_t st) {
+    int* err = (int*)ws;
+    unsigned* cnt = (ws && (int64_t)B * Hkv <= kWsCounters) ? (unsigned*)((char*)ws + kWsCounterOff) : nullptr;
     AttnArgs a{};
     a.q = (const bf16_t*)q; a.kc = (const bf16_t*)kc; a.vc = (const bf16_t*)vc; a.seqlens = seqlens;
     a.out = (bf16_t*)out; a.B = B; a.Sq = Sq; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.L_max = L_max;
     a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
-    a.causal = causal; a.nsplit = nsplit; a.part = part; a.err = err;
+    a.causal = causal; a.nsplit = nsplit; a.part = part; a.cnt = cnt; a.err = err;
     if (Sq == 1) return launch_attn_decode(a, st);
     return launch_attn_prefill(a, st);
 }
@@ -546,7 +549,7 @@ fsvd_status_t enqueue_layer(const fsvd_decoder_layer_desc* d, hipStream_t st) {
     TRY(enqueue_qkv(qd, d->x, folded || d->attn_norm_w != nullptr, folded ? nullptr : d->attn_norm_w, d->A_qkv, d->Vt_q, d->Vt_k, d->Vt_v, p.q, d->k_cache, d->v_cache,
                     d->cache_seqlens, nullptr, nullptr, p.qb, st));
     TRY(enqueue_attn(p.q, d->k_cache, d->v_cache, d->L_max, d->cache_seqlens, B, S, (int)d->Hq, (int)d->Hkv,
-                     (int)d->D, d->softmax_scale, 1, p.o, p.attn_part, p.nsplit, p.qb.err, st));
+                     (int)d->D, d->softmax_scale, 1, p.o, p.attn_part, p.nsplit, d->ws, st));
     const int qdim = (int)(d->Hq * d->D);
     LinearBufs lb{p.z_o, p.qb.err, p.part};
     TRY(enqueue_linear(p.o, M, qdim, qdim, d->Ut_o, (int)d->r_o, qdim, d->Vt_o, (int)d->d, d->r_o, nullptr, d->x, d->d,
@@ -858,7 +861,7 @@ fsvd_status_t fsvd_decode_attn_dense_kv(const void* q, const void* k_cache, cons
     Carve c(ws);
     float* part = (float*)c.take(attn_decode_ws_bytes((int)B, (int)Hq, (int)D, ns));
     return enqueue_attn(q, k_cache, v_cache, L_max, cache_seqlens, (int)B, (int)Sq, (int)Hq, (int)Hkv, (int)D,
-                        softmax_scale, causal, out, part, ns, (int*)ws, (hipStream_t)stream);
+                        softmax_scale, causal, out, part, ns, ws, (hipStream_t)stream);
 }
 
 size_t fsvd_decode_attn_lowrank_kv_ws(int64_t B, int64_t Sq, int64_t Hq, int64_t Hkv, int64_t D, int64_t L_max) {
@@ -911,7 +914,7 @@ fsvd_status_t fsvd_decode_attn_lowrank_kv(const void* q, const void* zk_cache, c
         TRY(launch_gemm(h, GEPI_QKV, st));
     }
     return enqueue_attn(q, kc, vc, L_max, cache_seqlens, (int)B, (int)Sq, (int)Hq, (int)Hkv, (int)D, softmax_scale,
-                        causal, out, part, ns, (int*)ws, st);
+                        causal, out, part, ns, ws, st);
 }
 
 fsvd_status_t fsvd_attn_factorized(const void* zq, const void* zk, const void* zv, int64_t ldz, const void* Vt_q,

@@ -179,7 +179,12 @@ __device__ __forceinline__ void set_dev_error(int* err, int bits) {
 // ------------------------------------------------------------------ host-side plumbing
 
 namespace fsvd {
-constexpr size_t kWsHeader = 256;
+// Workspace header: the device error word (int32 at offset 0), then from kWsCounterOff the decode
+// attention's per-(sequence, kv head) partition counters, which only the attention kernels write
+// and which every call leaves at zero.
+constexpr size_t kWsHeader = 4096;
+constexpr size_t kWsCounterOff = 64;
+constexpr int kWsCounters = (int)((kWsHeader - kWsCounterOff) / 4);
 
 void set_error(const char* fmt, ...);
 fsvd_status_t fail(fsvd_status_t s, const char* fmt, ...);

@@ -88,6 +88,8 @@ struct AttnArgs {
     int causal;
     int nsplit;        // decode: partitions of the length
     float* part;       // decode partials [B, Hq, nsplit, D + 2]
+    unsigned* cnt;     // decode: [B * Hkv] partition counters (zero on entry, zero on exit); the
+                       // last partition of each (b, kv head) merges them.  Null: a second kernel merges
     int* err;
     int pos_off;       // Sq > 1: query s of sequence b sits at position seqlens[b] + pos_off + s (a
                        // prefill chunk that starts pos_off tokens into the call's new tokens)

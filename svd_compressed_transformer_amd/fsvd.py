@@ -139,7 +139,8 @@ def dtype_of(t) -> int:
 
 
 def workspace(nbytes: int, device="cuda"):
-    """A zero-filled byte workspace (the header's device error word must start at zero)."""
+    """A zero-filled byte workspace (its header, the device error word and the decode attention's
+    partition counters, must start at zero)."""
     import torch
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 

@@ -10,6 +10,7 @@ import pytest
 from svd_compressed_transformer_amd import fsvd
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = 4096  # workspace header: the device error word, then the decode attention's partition counters
 
 
 def declared_functions():
@@ -46,13 +47,13 @@ def test_version_and_status_strings(L):
 
 def test_workspace_queries(L):
     # header + 256-aligned z: M * r * 2 bytes
-    assert fsvd.fsvd_lowrank_linear_ws(4, 4096, 1640, 4096, fsvd.FSVD_BF16) == 256 + ((4 * 1640 * 2 + 255) // 256) * 256
-    assert fsvd.fsvd_lowrank_linear_ws(16, 256, 64, 256, fsvd.FSVD_F32) == 256 + 16 * 64 * 4
-    assert fsvd.fsvd_decode_attn_dense_kv_ws(4, 1, 32, 32, 128, 2176) > 256
-    assert fsvd.fsvd_lowrank_qkv_ws(1, 1, 4096, 1640, 1640, 1640, 32, 32, 128) >= 256 + 4920 * 2
+    assert fsvd.fsvd_lowrank_linear_ws(4, 4096, 1640, 4096, fsvd.FSVD_BF16) == HDR + ((4 * 1640 * 2 + 255) // 256) * 256
+    assert fsvd.fsvd_lowrank_linear_ws(16, 256, 64, 256, fsvd.FSVD_F32) == HDR + 16 * 64 * 4
+    assert fsvd.fsvd_decode_attn_dense_kv_ws(4, 1, 32, 32, 128, 2176) > HDR
+    assert fsvd.fsvd_lowrank_qkv_ws(1, 1, 4096, 1640, 1640, 1640, 32, 32, 128) >= HDR + 4920 * 2
     d = fsvd.decoder_layer_desc(B=4, S=1, d=4096, Hq=32, Hkv=32, D=128, d_ff=11008, L_max=2176, r_q=1640, r_k=1640,
                                 r_v=1640, r_o=1640, r_g=1640, r_u=1640, r_d=1640)
-    assert fsvd.fsvd_decoder_layer_ws(d) > 256
+    assert fsvd.fsvd_decoder_layer_ws(d) > HDR
 
 
 def test_mlp_workspace_keeps_t_on_chip(L):
@@ -64,15 +65,15 @@ def test_mlp_workspace_keeps_t_on_chip(L):
     M, d, dff = 4096, 768, 3072
     common = al(M * d * 2) + al(M * 4)  # normalised input and its per-row rstd (MFMA path)
     r = 384
-    assert fsvd.fsvd_lowrank_mlp_packed_ws(M, d, 0, r, dff, r) == 256 + al(M * r * 2) + al(8 * M * r * 2) + al(M * r * 2) + common
+    assert fsvd.fsvd_lowrank_mlp_packed_ws(M, d, 0, r, dff, r) == HDR + al(M * r * 2) + al(8 * M * r * 2) + al(M * r * 2) + common
     r = 392
-    assert fsvd.fsvd_lowrank_mlp_packed_ws(M, d, 0, r, dff, r) == 256 + al(M * r * 2) + al(M * dff * 2) + al(M * r * 2) + common
+    assert fsvd.fsvd_lowrank_mlp_packed_ws(M, d, 0, r, dff, r) == HDR + al(M * r * 2) + al(M * dff * 2) + al(M * r * 2) + common
     # one slice when the row blocks alone fill the chip: z_d written directly, no partials
     M = 16600
     common = al(M * 256 * 2) + al(M * 4)
-    assert fsvd.fsvd_lowrank_mlp_packed_ws(M, 256, 0, 128, 264, 128) == 256 + 2 * al(M * 128 * 2) + common
+    assert fsvd.fsvd_lowrank_mlp_packed_ws(M, 256, 0, 128, 264, 128) == HDR + 2 * al(M * 128 * 2) + common
     # decode sizes keep the two-kernel path (t of a few rows stays in L2)
-    assert fsvd.fsvd_lowrank_mlp_packed_ws(16, d, 0, 384, dff, 384) >= 256 + al(16 * dff * 2)
+    assert fsvd.fsvd_lowrank_mlp_packed_ws(16, d, 0, 384, dff, 384) >= HDR + al(16 * dff * 2)
 
 
 def _status(f):

@@ -318,6 +318,54 @@ def test_attention_decode(B, Hq, Hkv, D, L_max, seqlens, qs):
     assert fsvd.fsvd_poll_device_error(ws) == 0
 
 
+def test_attention_decode_merge_counters_reset_and_shared_workspace():
+    """The last partition of each (sequence, kv head) merges the partitions, counted in the
+    workspace header.  One workspace serves repeated calls, with a projection call sharing it in
+    between (its slices lie past the header): every result matches the oracle, repeats are bit
+    identical whichever partition finishes last, and every call leaves the counters at zero."""
+    B, Hq, Hkv, D, L_max = 4, 32, 32, 128, 2300
+    sl = [2048, 100, 2299, 7]
+    nb_attn = fsvd.fsvd_decode_attn_dense_kv_ws(B, 1, Hq, Hkv, D, L_max)
+    M, K, r, N = 9, 4096, 1640, 4096
+    nb = max(nb_attn, fsvd.fsvd_lowrank_linear_ws(M, K, r, N, fsvd.FSVD_BF16))
+    ws = fsvd.workspace(nb)
+    x, Ut, Vt, _, _ = _linear_case(M, K, r, N, "bf16", seed=3)
+    xd, Ud, Vd = to_dev(x), to_dev(Ut), to_dev(Vt)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    slt = torch.from_numpy(np.asarray(sl, dtype=np.int32)).cuda()
+    counters = lambda: ws[64:64 + 4 * B * Hkv].view(torch.int32)
+    first = None
+    for call, seed in enumerate([5, 6, 5]):
+        say("attn merge counters, call", call)
+        q, kc, vc, _ = I.make_attention_case(B, 1, Hq, Hkv, D, L_max, sl, seed=seed, q_scale=8.0)
+        out = torch.empty((B, 1, Hq, D), dtype=torch.bfloat16, device="cuda")
+        fsvd.fsvd_decode_attn_dense_kv(to_dev(q), to_dev(kc), to_dev(vc), L_max, slt, B, 1, Hq, Hkv, D, 0.0, 1, out,
+                                       fsvd.FSVD_BF16, ws, nb)
+        torch.cuda.synchronize()
+        assert int(counters().abs().sum()) == 0
+        assert rel(from_dev(out), O.attention(q, kc, vc, sl, causal=True)) <= BF16_TOL
+        if call == 0:
+            first = out.clone()
+            fsvd.fsvd_lowrank_linear(xd, M, K, K, Ud, r, K, Vd, N, r, None, None, N, y, N, fsvd.FSVD_BF16, ws, nb)
+            torch.cuda.synchronize()
+            assert rel(from_dev(y), O.lowrank_linear(x, Ut, Vt)) <= BF16_TOL
+        if call == 2:
+            assert torch.equal(out, first)
+    assert fsvd.fsvd_poll_device_error(ws) == 0
+
+
+def test_attention_decode_beyond_header_counters():
+    """B * Hkv above the header's 1008 partition counters: a second kernel merges the partitions."""
+    B, Hq, Hkv, D, L_max = 64, 16, 16, 64, 96
+    rng = np.random.default_rng(9)
+    sl = [int(v) for v in rng.integers(0, L_max, size=B)]
+    say("attn decode, B * Hkv = 1024")
+    q, kc, vc, _ = I.make_attention_case(B, 1, Hq, Hkv, D, L_max, sl, q_scale=4.0)
+    o, ws = _run_attn(q, kc, vc, sl, True, L_max, Hkv)
+    assert rel(o, O.attention(q, kc, vc, sl, causal=True)) <= BF16_TOL
+    assert fsvd.fsvd_poll_device_error(ws) == 0
+
+
 def test_attention_decode_poisoned_tail_not_read():
     B, Hq, Hkv, D, L_max = 2, 4, 2, 128, 200
     sl = [50, 120]
