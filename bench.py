@@ -516,7 +516,7 @@ def main():
                    "hbm_frac_of_measured_read": round(dec_gbs / read_gbs, 4),
                    "one_graph_per_step": {"ms": round(t_dec_stack_ms, 3),
                                           "us_per_layer_step": round(t_dec_stack_ms * 1e3 / (ND * NL), 2)}},
-        "roofline": {"bound": "hbm", "kernel": "attn_decode_split (+combine)", "achieved": round(attn_gbs, 1),
+        "roofline": {"bound": "hbm", "kernel": "attn_decode_split", "achieved": round(attn_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(), "avg_us": round(attn_us, 2),
                      "algorithmic_bytes": int(attn_bytes), "kv_positions": int(L_mid),
