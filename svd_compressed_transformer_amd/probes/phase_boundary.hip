@@ -19,6 +19,9 @@
 // per CU holds fewer loads in flight than the many-workgroup kernels).
 //   lds_prefetch: contiguous shares per workgroup, the first 128 KB of the next phase's share
 //             prefetched into LDS with global -> LDS loads while the current phase finishes.
+//   kernels9: the layer-step with the attention partitions merged inside the attention kernel (the
+//             2.2 MB merge phase gone, the attention phase at 512 workgroups); then the same 9
+//             phases with every grid at 512, 1024 and 2048 workgroups.
 //
 // Every activation word encodes (layer-step, phase, slot); each reader counts the words it does not
 // find as expected, which the run reports (a stale read would show there).  Every spin is bounded:
@@ -39,6 +42,7 @@ constexpr int PF = 8;            // prefetched 16-byte vectors per thread
 // phase sizes in MB (Llama-7B decode at batch 4, algorithmic bytes) and the decode kernels' grids
 constexpr double MB[P] = {40.26, 40.26, 138.45, 2.2, 13.42, 13.42, 26.84, 72.13, 36.06, 13.42};
 constexpr int GRID[P] = {1248, 1536, 4096, 128, 416, 512, 832, 2752, 416, 512};
+constexpr int GRID9[P] = {1248, 1536, 512, 0, 416, 512, 832, 2752, 416, 512};  // 0: phase not run
 
 struct Phases {
     const u32x4* w[P];
@@ -80,10 +84,11 @@ __device__ __forceinline__ void write_act(uint32_t* act, uint32_t step, int p) {
     }
 }
 
-// one phase as its own kernel: activation in, share of the stream, activation slice out
+// one phase as its own kernel: activation in (that of phase p - skip - 1), share of the stream,
+// activation slice out
 __global__ __launch_bounds__(256) void phase_kernel(const u32x4* __restrict__ w, long n16, uint32_t* act, int p,
-                                                    uint32_t step, unsigned* bad, uint32_t* sink) {
-    read_act<false>(act, step, p, bad);
+                                                    uint32_t step, unsigned* bad, uint32_t* sink, int skip = 0) {
+    read_act<false>(act, step, p - skip, bad);
     const long stride = (long)gridDim.x * blockDim.x;
     long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     uint32_t acc = 0;
@@ -281,19 +286,29 @@ int main() {
     // each copy's graph is captured with a fixed step and the activation check tolerates reuse by
     // writing before reading within the same graph (phase 0 reads nothing)
     CK(hipFuncSetAttribute((const void*)persist_lds_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, LDSV * 16));
-    for (int variant = 0; variant < 6; ++variant) {
+    constexpr int NV = 10;
+    for (int variant = 0; variant < NV; ++variant) {
         std::vector<float> v;
         for (int rep = 0; rep < 5; ++rep) {
             CK(hipMemsetAsync(xcnt, 0, 8 * 32 * 4, st)); CK(hipMemsetAsync(gcnt, 0, 4, st));
             CK(hipMemsetAsync(bad, 0, 4, st)); CK(hipMemsetAsync(err, 0, 4, st));
             CK(hipStreamSynchronize(st));
             std::vector<hipGraphExec_t> ge;
-            if (variant == 0) {
+            const bool graphs = variant == 0 || variant >= 6;
+            if (graphs) {
                 for (int l = 0; l < NL; ++l) {
                     hipGraph_t g;
                     CK(hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal));
-                    for (int p = 0; p < P; ++p)
-                        phase_kernel<<<GRID[p], 256, 0, st>>>(ph[l].w[p], n16[p], act, p, (uint32_t)l, bad, sink);
+                    for (int p = 0, skip = 0; p < P; ++p) {
+                        if (variant == 0) {
+                            phase_kernel<<<GRID[p], 256, 0, st>>>(ph[l].w[p], n16[p], act, p, (uint32_t)l, bad, sink);
+                            continue;
+                        }
+                        if (GRID9[p] == 0) { skip = 1; continue; }
+                        const int grid = variant == 6 ? GRID9[p] : variant == 7 ? 512 : variant == 8 ? 1024 : 2048;
+                        phase_kernel<<<grid, 256, 0, st>>>(ph[l].w[p], n16[p], act, p, (uint32_t)l, bad, sink, skip);
+                        skip = 0;
+                    }
                     CK(hipStreamEndCapture(st, &g));
                     hipGraphExec_t x;
                     CK(hipGraphInstantiate(&x, g, nullptr, nullptr, 0));
@@ -306,7 +321,7 @@ int main() {
             CK(hipEventRecord(e0, st));
             for (int s = 0; s < steps; ++s) {
                 const int l = s % NL;
-                if (variant == 0) {
+                if (graphs) {
                     CK(hipGraphLaunch(ge[l], st));
                 } else {
                     const unsigned kbase = (unsigned)s * (P - 1);  // barriers before this step
@@ -339,9 +354,11 @@ int main() {
         }
         std::sort(v.begin(), v.end());
         const double us = v[2] * 1e3 / steps;
-        const char* name[6] = {"kernels", "persist", "prefetch", "persist_depth16", "prefetch_depth16", "lds_prefetch"};
+        const char* name[NV] = {"kernels", "persist", "prefetch", "persist_depth16", "prefetch_depth16", "lds_prefetch",
+                                "kernels9", "kernels9_grid512", "kernels9_grid1024", "kernels9_grid2048"};
+        const double vb = variant >= 6 ? bytes - (double)n16[3] * 16 : bytes;  // the 9 phases skip the merge's bytes
         printf("{\"variant\": \"%s\", \"us_per_layer_step\": %.2f, \"gbs\": %.1f, \"of_8tbs\": %.3f}\n", name[variant], us,
-               bytes / (us * 1e-6) / 1e9, bytes / (us * 1e-6) / 8e12);
+               vb / (us * 1e-6) / 1e9, vb / (us * 1e-6) / 8e12);
     }
     return 0;
 }
