@@ -3,8 +3,9 @@
 // At prefill the two phases of y = (x . U) . V are dense contractions with M = B*S in the
 // thousands (about M flop per factor byte, far above the MFMA ridge), so each phase runs as an
 // NT GEMM C[M, N] = A[M, K] . B[N, K]^T on the matrix cores with a fused epilogue:
-//   - tiles of BM x BN (256 x 256 down to 64 x 128, the largest that still fills the chip), four
-//     waves as 2 x 2, each wave a grid of 32 x 32 blocks computed with
+//   - tiles of BM x BN (256 x 256 down to 64 x 128, the largest that still fills the chip; short
+//     reductions take 128 x 192 or 64 x 128), four waves as 2 x 2, each wave a grid of 32 x 32
+//     blocks computed with
 //     v_mfma_f32_32x32x16_bf16 (fp32 accumulation);
 //   - operands move global -> LDS directly (global_load_lds_dwordx4, no staging registers) through
 //     a 3- or 4-stage pipeline of BK = 64 or 32 slices (BK = 64: one whole 128-byte line per row
@@ -425,7 +426,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
     // processed, so the passes do not wait on them one by one.
     constexpr int LPR = T::WN / 8;         // lanes per row
     constexpr int RP = 64 / LPR;           // rows per pass
-    constexpr int NP = 32 / RP;            // passes per 32-row block
+    constexpr int NP = (32 + RP - 1) / RP; // passes per 32-row block
+    // with 96-wide wave tiles 12 lanes cover a row: 5 rows per pass, lanes 60-63 idle, and the
+    // seventh pass covers the last 2 rows
+    const bool lane_on = lane < RP * LPR;
     const int c8 = (lane % LPR) * 8;
     const int col = wn + c8;
     const bool full = col + 8 <= g.N;
@@ -452,8 +456,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
     auto prefetch = [&](int i, u32x4 (&rv)[NP], float (&rs)[NP]) {
 #pragma unroll
         for (int pass = 0; pass < NP; ++pass) {
-            const int row = wm + i * 32 + pass * RP + lane / LPR;
-            const bool ok = row < g.M && col < g.N;
+            const int r = pass * RP + lane / LPR;
+            const int row = wm + i * 32 + r;
+            const bool ok = lane_on && r < 32 && row < g.M && col < g.N;
             rs[pass] = (EPI != GEPI_SWIGLU && g.rstd && ok) ? g.rstd[row] : 1.0f;
             rv[pass] = u32x4{0u, 0u, 0u, 0u};
             if constexpr (EPI == GEPI_LINEAR) {
@@ -471,7 +476,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs g) {
         for (int pass = 0; pass < NP; ++pass) {
             const int r = pass * RP + lane / LPR;
             const int row = wm + i * 32 + r;
-            if (row >= g.M || col >= g.N) continue;
+            if (!lane_on || r >= 32 || row >= g.M || col >= g.N) continue;
             float y[8];
             ld8(r, c8, y);
             if constexpr (EPI != GEPI_SWIGLU) {
@@ -565,6 +570,20 @@ fsvd_status_t launch_epi(const GemmArgs& g, hipStream_t st) {
             return launch_t<64, 128, EPI>(g, st);
         } else {
             if (tiles(256, 256) >= 200) return launch_t<256, 256, EPI>(g, st);
+            // Short reductions (K <= 1024, the BERT-Base-sized projections): a tile's prologue and
+            // epilogue are a large share of its time, so the tiles that win either let two
+            // workgroups share a CU (64 x 128, 72 KiB of LDS), each hiding the other's, or fill
+            // the CUs in one round (128 x 192).  Measured on MI355X at M = 4096: Q/K/V phase 1
+            // (N 1152, K 768) 16.7 us on 128 x 192 against 21.7 on 128 x 128 and 17.7 on
+            // 64 x 128; the grouped Q/K/V phase 2 (3 x N 768, K 384, D 64) 19.3 us on 64 x 128
+            // against 24.0 on 128 x 256; N 384 and 768 fastest on 64 x 128.
+            if (g.K <= 1024 && !(EPI == GEPI_QKV && g.D > 64)) {
+                if constexpr (EPI == GEPI_STORE || EPI == GEPI_LINEAR) {
+                    if (g.N % 192 == 0 && tiles(128, 192) >= 160 && tiles(128, 192) <= 256)
+                        return launch_t<128, 192, EPI>(g, st);
+                }
+                return launch_t<64, 128, EPI>(g, st);
+            }
             if (tiles(128, 256) >= 256 || (EPI == GEPI_QKV && g.D > 64)) return launch_t<128, 256, EPI>(g, st);
         }
         if (tiles(128, 128) >= 256) return launch_t<128, 128, EPI>(g, st);

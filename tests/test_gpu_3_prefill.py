@@ -25,7 +25,10 @@ def say(*a):
 
 @pytest.mark.parametrize("M,K,r,N,extras", [(33, 256, 64, 256, False), (300, 1000, 40, 1032, True),
                                             (1000, 4096, 1640, 1672, False), (513, 768, 392, 3000, True),
-                                            (4096, 768, 384, 768, True)])
+                                            (4096, 768, 384, 768, True),
+                                            # 128 x 192 tiles (short reductions): phase 1 with a ragged
+                                            # last row tile, then phase 2 with bias and residual
+                                            (4001, 1000, 960, 1000, False), (3001, 1000, 768, 1536, True)])
 def test_linear_mfma(M, K, r, N, extras):
     say("mfma linear", M, K, r, N, extras)
     rng = np.random.default_rng(M)
