@@ -93,7 +93,7 @@ def decode_bytes(cfg, logical, B, L_read):
 
 
 def run_decode(B, history, ratio, layers, steps, dev, stream, one_graph=True):
-    L_max = history + steps + 1
+    L_max = (history + steps + 1 + 63) // 64 * 64  # cache rows: a multiple of 64 (sequence starts aligned)
     sl = torch.full((layers, B), history, dtype=torch.int32, device=dev)
     ys = [torch.randn((B, 1, D_MODEL), device=dev).to(torch.bfloat16) for _ in range(layers)]
     stack = []
