@@ -142,7 +142,7 @@ def workspace(nbytes: int, device="cuda"):
     """A zero-filled byte workspace (its header, the device error word and the decode attention's
     partition counters, must start at zero)."""
     import torch
-    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(int(nbytes), 4096), dtype=torch.uint8, device=device)
 
 
 # ----------------------------------------------------------------------------- the ABI calls
