@@ -47,9 +47,10 @@
  *     call says so (capture, poll).
  *   - Workspace: each call that needs scratch takes (ws, ws_bytes); the matching *_ws() query
  *     returns the size.  The first 4096 bytes of every workspace are a header: its first int32
- *     is the DEVICE ERROR WORD, and from byte 64 on it holds the decode attention's partition
- *     counters, which every call leaves at zero.  A workspace must be zero-filled once before
- *     its first use; after that the header stays valid whichever calls share the workspace.
+ *     is the DEVICE ERROR WORD, and from byte 64 on it holds counters of the decode kernels (the
+ *     split reductions' tiles, then the attention's partitions), which every call leaves at zero.
+ *     A workspace must be zero-filled once before its first use; after that the header stays
+ *     valid whichever calls share the workspace.
  *   - Errors: every call returns fsvd_status_t.  Arguments are validated before any launch
  *     (null pointers, non-positive sizes, misalignment, too-small workspace, unsupported
  *     combinations); on failure nothing is launched and fsvd_last_error() explains.  Launch
@@ -228,7 +229,7 @@ fsvd_status_t fsvd_lowrank_mlp_packed(const void* x, int64_t M, int64_t d,
  * softmax_scale 0 -> 1/sqrt(D).  Sq == 1 uses split-length partitions merged by log-sum-exp
  * (the partition count is fixed by the workspace; lengths are read on the device, so a
  * captured graph stays valid as the cache grows).  The last partition of each (sequence, kv
- * head) to finish does the merge, counted in the workspace header when B * Hkv <= 1008; beyond
+ * head) to finish does the merge, counted in the workspace header when B * Hkv <= 880; beyond
  * that a second kernel merges.  Sq > 1 (prefill and encoder layers) runs on the matrix cores.
  * D must be 64 or 128; Hq % Hkv == 0.  bf16 only.  Layout advice: L_max a multiple of 64 keeps each
  * sequence's cache on a 64-position boundary, which decode streams faster (MI355X, batch 4, 32 heads

@@ -179,11 +179,14 @@ __device__ __forceinline__ void set_dev_error(int* err, int bits) {
 // ------------------------------------------------------------------ host-side plumbing
 
 namespace fsvd {
-// Workspace header: the device error word (int32 at offset 0), then from kWsCounterOff the decode
-// attention's per-(sequence, kv head) partition counters, which only the attention kernels write
-// and which every call leaves at zero.
+// Workspace header: the device error word (int32 at offset 0), then two sets of counters that
+// every call leaves at zero: from kWsSplitCounterOff one per tile of a decode projection whose
+// reduction is split over workgroups (at most 128 tiles), from kWsCounterOff one per (sequence, kv
+// head) of the decode attention.  Only the kernels that count write them.
 constexpr size_t kWsHeader = 4096;
-constexpr size_t kWsCounterOff = 64;
+constexpr size_t kWsSplitCounterOff = 64;
+constexpr int kWsSplitCounters = 128;
+constexpr size_t kWsCounterOff = kWsSplitCounterOff + 4 * kWsSplitCounters;
 constexpr int kWsCounters = (int)((kWsHeader - kWsCounterOff) / 4);
 
 void set_error(const char* fmt, ...);

@@ -395,6 +395,9 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
 typedef __bf16 bf16x8_m __attribute__((ext_vector_type(8)));
 typedef float f32x4_m __attribute__((ext_vector_type(4)));
 constexpr int kMfmaRows = 16;  // factor rows per wave tile
+#ifndef FSVD_RD_COUNTED_SPLIT
+#define FSVD_RD_COUNTED_SPLIT 1  // 0: split reductions always finish in the second kernel (for comparisons)
+#endif
 constexpr int kMfmaSteps = 8;  // 32-wide k steps whose loads one pass keeps in flight (16 activation rows)
 // Factor rows of a pass staged through a wave-private LDS buffer with row-contiguous loads (an
 // instruction reads 512 or 256 contiguous bytes of each of 2 or 4 rows) instead of loading the
@@ -420,6 +423,39 @@ __device__ __forceinline__ RowdotSeg seg_of(const RowdotArgs& a, int blk) {
 __host__ __device__ inline int part_vals(int ngroups, int ns) { return ngroups * ns * kMfmaRows * 32 + ngroups * 32; }
 __host__ __device__ inline int part_val_idx(int g, int h, int r, int m, int ns) { return ((g * ns + h) * kMfmaRows + r) * 32 + m; }
 __host__ __device__ inline int part_ss_idx(int g, int m, int ngroups, int ns) { return ngroups * ns * kMfmaRows * 32 + g * 32 + m; }
+
+// Finishes tile blk of a split reduction: sums its kpart partial tiles in part order and runs the
+// epilogue of the unsplit kernel on them (same threads, same unit mapping).  COHERENT: the partials
+// were written in the same kernel by workgroups on any XCD, so they are read with agent-scope loads.
+template <int EPI, bool COHERENT>
+__device__ __forceinline__ void finish_split_tile(const RowdotArgs& a, int blk, int tid) {
+    using T = bf16_t;
+    const RowdotSeg sg = seg_of<EPI>(a, blk);
+    constexpr int NS = EPI == EPI_SWIGLU ? 2 : 1;
+    const bool paired = seg_paired(EPI, sg.kind);
+    const int upw = paired ? kMfmaRows / 2 : kMfmaRows;
+    const int n_units = (EPI == EPI_QKV && paired) ? sg.N / 2 : sg.N;
+    const int ngroups = a.waves / (NS * a.ksplit);
+    const int nv = part_vals(ngroups, NS);
+    const float* src = a.part + (int64_t)blk * nv;
+    const int64_t pstride = (int64_t)a.nblk * nv;
+    auto sum_parts = [&](int idx) -> float {
+        float s = 0.f;
+        for (int p = 0; p < a.kpart; ++p) {
+            const float* e = src + p * pstride + idx;
+            if constexpr (COHERENT) s += __hip_atomic_load(e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else s += *e;
+        }
+        return s;
+    };
+    auto val = [&](int g, int h, int r, int m) -> float { return sum_parts(part_val_idx(g, h, r, m, NS)); };
+    auto ssq = [&](int g, int m) -> float { return sum_parts(part_ss_idx(g, m, ngroups, NS)); };
+    if constexpr (EPI == EPI_LINEAR) {
+        if (a.adv_seqlens != nullptr && blk == 0 && tid < a.adv_B) a.adv_seqlens[tid] += a.adv_n;
+    }
+    rowdot_epilogue<T, EPI>(a, sg, (blk - sg.blk_begin) * sg.units_per_blk, ngroups, upw, kMfmaRows / 2, n_units, tid,
+                            64 * a.waves, val, ssq);
+}
 
 template <int MB, int EPI, bool DB>
 __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
@@ -611,7 +647,7 @@ __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
         return sum_waves(g * NS * ksplit, [&](int w) { return red_ss[w][m]; });
     };
     const int ngroups = a.waves / (NS * ksplit);
-    if (a.kpart > 1) {  // partial tile of this reduction part; rowdot_part_reduce finishes it
+    if (a.kpart > 1) {  // partial tile of this reduction part
         const int nv = part_vals(ngroups, NS);
         float* dst = a.part + ((int64_t)kp * a.nblk + bid) * nv;
         for (int idx = tid; idx < nv; idx += 64 * a.waves) {
@@ -624,8 +660,25 @@ __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
                 const int m = (idx - nval) % 32, g = (idx - nval) / 32;
                 v = (norm && m < a.M) ? ssq(g, m) : 0.f;
             }
-            dst[idx] = v;
+            // agent-scope store: written through to the level every XCD reads coherently
+            __hip_atomic_store(dst + idx, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        if (a.split_cnt == nullptr) return;  // rowdot_part_reduce finishes the tile
+        // The last of the tile's kpart workgroups to finish sums the partials.  Every thread waits
+        // until its partial stores have completed before the barrier, and only then is the part
+        // counted, so the workgroup that takes the last count reads every part back with agent-scope
+        // loads.  Nothing waits on another workgroup.  The counter is reset for the next launch.
+        __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+        __syncthreads();
+        __shared__ int is_last;
+        if (tid == 0) {
+            const unsigned old = __hip_atomic_fetch_add(a.split_cnt + bid, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const bool last = old + 1 == (unsigned)a.kpart;
+            if (last) __hip_atomic_store(a.split_cnt + bid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            is_last = last;
+        }
+        __syncthreads();
+        if (is_last) finish_split_tile<EPI, true>(a, bid, tid);
         return;
     }
     if constexpr (EPI == EPI_LINEAR) {
@@ -635,33 +688,10 @@ __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
                             64 * a.waves, val, ssq);
 }
 
-// Second kernel of a split reduction: workgroup blk sums the kpart partial tiles of tile blk and
-// runs the epilogue of the unsplit kernel on them (same threads, same unit mapping).
+// Second kernel of a split reduction (no counters): workgroup blk finishes tile blk.
 template <int EPI>
 __global__ __launch_bounds__(512) void rowdot_part_reduce(const RowdotArgs a) {
-    using T = bf16_t;
-    const int tid = threadIdx.x, bid = blockIdx.x;
-    const RowdotSeg sg = seg_of<EPI>(a, bid);
-    constexpr int NS = EPI == EPI_SWIGLU ? 2 : 1;
-    const bool paired = seg_paired(EPI, sg.kind);
-    const int upw = paired ? kMfmaRows / 2 : kMfmaRows;
-    const int n_units = (EPI == EPI_QKV && paired) ? sg.N / 2 : sg.N;
-    const int ngroups = a.waves / (NS * a.ksplit);
-    const int nv = part_vals(ngroups, NS);
-    const float* src = a.part + (int64_t)bid * nv;
-    const int64_t pstride = (int64_t)a.nblk * nv;
-    auto sum_parts = [&](int idx) -> float {
-        float s = 0.f;
-        for (int p = 0; p < a.kpart; ++p) s += src[p * pstride + idx];
-        return s;
-    };
-    auto val = [&](int g, int h, int r, int m) -> float { return sum_parts(part_val_idx(g, h, r, m, NS)); };
-    auto ssq = [&](int g, int m) -> float { return sum_parts(part_ss_idx(g, m, ngroups, NS)); };
-    if constexpr (EPI == EPI_LINEAR) {
-        if (a.adv_seqlens != nullptr && bid == 0 && tid < a.adv_B) a.adv_seqlens[tid] += a.adv_n;
-    }
-    rowdot_epilogue<T, EPI>(a, sg, (bid - sg.blk_begin) * sg.units_per_blk, ngroups, upw, kMfmaRows / 2, n_units, tid,
-                            64 * a.waves, val, ssq);
+    finish_split_tile<EPI, false>(a, (int)blockIdx.x, (int)threadIdx.x);
 }
 
 template <typename T, int EPI>
@@ -772,7 +802,7 @@ fsvd_status_t launch_mfma(const RowdotArgs& a, int grid, hipStream_t st) {
         const bool db = (steps + mfma_pass_steps<2>() - 1) / mfma_pass_steps<2>() >= 3;
         s = db ? launch_mfma_t<2, EPI, true>(a, grid, st) : launch_mfma_t<2, EPI, false>(a, grid, st);
     }
-    if (s != FSVD_OK || a.kpart <= 1) return s;
+    if (s != FSVD_OK || a.kpart <= 1 || a.split_cnt) return s;
     rowdot_part_reduce<EPI><<<a.nblk, 64 * a.waves, 0, st>>>(a);
     return check_launch("rowdot_part_reduce");
 }
@@ -793,6 +823,10 @@ fsvd_status_t launch_rowdot(const RowdotArgs& a, int epi, fsvd_dtype_t dtype, hi
     if (c.M < 1 || c.M > 32) return fail(FSVD_ERR_UNSUPPORTED, "row-dot path supports 1..32 activation rows, got %d", c.M);
     const int grid = rowdot_plan(c, epi, dtype);
     if (grid <= 0) return FSVD_OK;
+    // a split reduction counts its finished parts in the workspace header (err is its first word)
+    c.split_cnt = (FSVD_RD_COUNTED_SPLIT && c.kpart > 1 && c.err != nullptr && c.nblk <= kWsSplitCounters)
+                      ? reinterpret_cast<unsigned*>(reinterpret_cast<char*>(c.err) + kWsSplitCounterOff)
+                      : nullptr;
     if (dtype == FSVD_F32) {
         switch (epi) {
             case EPI_Z: return launch_b<float, EPI_Z>(c, grid, st);

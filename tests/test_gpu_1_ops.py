@@ -134,6 +134,28 @@ def test_linear_bias_residual_inplace(dtype, M):
     assert rel(_run_linear(x, Ut, Vt, b, res, dtype, inplace=True), ref) <= tol
 
 
+def test_linear_split_reduction_counters():
+    """9 rows on the matrix cores: phase 1 (1640 outputs, K 4096) has few tiles and splits its
+    reduction over 2 workgroups per tile; the last of each tile's workgroups to finish sums the
+    parts, counted in the workspace header.  Two calls on one workspace: parity with the oracle,
+    bit-identical repeats, and the counters back at zero after each call."""
+    M, K, r, N = 9, 4096, 1640, 4096
+    x, Ut, Vt, _, _ = _linear_case(M, K, r, N, "bf16", seed=11)
+    xd, Ud, Vd = to_dev(x), to_dev(Ut), to_dev(Vt)
+    nb = fsvd.fsvd_lowrank_linear_ws(M, K, r, N, fsvd.FSVD_BF16)
+    ws = fsvd.workspace(nb)
+    outs = []
+    for call in range(2):
+        say("split-reduction linear, call", call)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        fsvd.fsvd_lowrank_linear(xd, M, K, K, Ud, r, K, Vd, N, r, None, None, N, y, N, fsvd.FSVD_BF16, ws, nb)
+        torch.cuda.synchronize()
+        assert int(ws[64:64 + 4 * 128].view(torch.int32).abs().sum()) == 0
+        outs.append(y)
+    assert rel(from_dev(outs[0]), O.lowrank_linear(x, Ut, Vt)) <= BF16_TOL
+    assert torch.equal(outs[0], outs[1])
+
+
 @pytest.mark.parametrize("M", [8, 24])
 def test_linear_deterministic(M):
     x, Ut, Vt, _, _ = _linear_case(M, 4096, 1640, 4096, "bf16", seed=1)
@@ -333,7 +355,7 @@ def test_attention_decode_merge_counters_reset_and_shared_workspace():
     xd, Ud, Vd = to_dev(x), to_dev(Ut), to_dev(Vt)
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     slt = torch.from_numpy(np.asarray(sl, dtype=np.int32)).cuda()
-    counters = lambda: ws[64:64 + 4 * B * Hkv].view(torch.int32)
+    counters = lambda: ws[576:576 + 4 * B * Hkv].view(torch.int32)  # after the 128 split-reduction counters
     first = None
     for call, seed in enumerate([5, 6, 5]):
         say("attn merge counters, call", call)
@@ -355,7 +377,7 @@ def test_attention_decode_merge_counters_reset_and_shared_workspace():
 
 
 def test_attention_decode_beyond_header_counters():
-    """B * Hkv above the header's 1008 partition counters: a second kernel merges the partitions."""
+    """B * Hkv above the header's 880 partition counters: a second kernel merges the partitions."""
     B, Hq, Hkv, D, L_max = 64, 16, 16, 64, 96
     rng = np.random.default_rng(9)
     sl = [int(v) for v in rng.integers(0, L_max, size=B)]
