@@ -53,14 +53,20 @@ struct KV {
     uint32_t w[EPL / 2];
 };
 
-template <int EPL>
+// STREAM: the K/V history, read once per call: non-temporal loads, so the stream does not take
+// the caches from the rest (measured on MI355X, batch 4, 32 heads of 128, 2112 positions: 25.1 us
+// per call against 28.0 us with plain loads; batch 16: 85.4 against 98.2 us)
+template <int EPL, bool STREAM = false>
 __device__ __forceinline__ KV<EPL> ld_kv(const bf16_t* p) {
     KV<EPL> r;
     if constexpr (EPL == 8) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        const u32x4 v = STREAM ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p))
+                               : *reinterpret_cast<const u32x4*>(p);
         r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
     } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 v = STREAM ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p))
+                               : *reinterpret_cast<const u32x2*>(p);
         r.w[0] = v.x; r.w[1] = v.y;
     }
     return r;
@@ -160,8 +166,8 @@ __global__ __launch_bounds__(256) void attn_decode_split(const AttnArgs a) {
         for (int p = 0; p < NP; ++p) {
             const int64_t j = jb + 16 * p;
             const int64_t jj = j < j1 ? j : j0;
-            kk[p] = ld_kv<EPL>(kbase + jj * rowstride);
-            vk[p] = ld_kv<EPL>(vbase + jj * rowstride);
+            kk[p] = ld_kv<EPL, true>(kbase + jj * rowstride);
+            vk[p] = ld_kv<EPL, true>(vbase + jj * rowstride);
         }
     };
     const int niter = j1 > j0 ? (int)((j1 - j0 + 16 * NP - 1) / (16 * NP)) : 0;  // uniform
