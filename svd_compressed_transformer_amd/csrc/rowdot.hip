@@ -395,6 +395,7 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
 typedef __bf16 bf16x8_m __attribute__((ext_vector_type(8)));
 typedef float f32x4_m __attribute__((ext_vector_type(4)));
 constexpr int kMfmaRows = 16;  // factor rows per wave tile
+constexpr int kAuxNonTemporal = 2;  // cache-policy operand of the direct-to-LDS load: nt
 #ifndef FSVD_RD_COUNTED_SPLIT
 #define FSVD_RD_COUNTED_SPLIT 1  // 0: split reductions always finish in the second kernel (for comparisons)
 #endif
@@ -552,8 +553,10 @@ __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
         for (int i = 0; i < NI; ++i) {
             const int sl = i * 64 + lane, j = sl / CPR, c = (sl % CPR) ^ j;
             const int k = min(k_lo + p * U * SE + c * 8, kc_max);
+            // factor rows are read once: the non-temporal policy bit (measured on MI355X, batch 8
+            // layer-step 147.9 -> 144.6 us, batch 16 203.5 -> 201.3 us)
             __builtin_amdgcn_global_load_lds((const void*)(row_ptr(j) + (int64_t)k * sizeof(T)),
-                                             (lds_void_rd*)(dst + i * 64), 16, 0, 0);
+                                             (lds_void_rd*)(dst + i * 64), 16, 0, kAuxNonTemporal);
         }
     };
     if (npass > 0) stage(0, stg);
