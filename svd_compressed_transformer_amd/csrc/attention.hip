@@ -22,6 +22,7 @@ namespace fsvd {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kAuxNonTemporal = 2;  // cache-policy operand of a buffer load: nt
 constexpr float kNegBig = -1.0e30f;
 #ifndef FSVD_ATTN_WGS
 // decode: target workgroups (sequence x kv head x length partition).  Few long partitions beat
@@ -153,6 +154,15 @@ __global__ __launch_bounds__(256) void attn_decode_split(const AttnArgs a) {
     const int64_t rowstride = (int64_t)a.Hkv * D;
     const bf16_t* kbase = a.kc + ((int64_t)b * a.L_max * a.Hkv + kvh) * D + li * EPL;
     const bf16_t* vbase = a.vc + ((int64_t)b * a.L_max * a.Hkv + kvh) * D + li * EPL;
+    // Grouped heads (G > 1, 128-wide heads) read K/V through buffer loads: a 32-bit offset per lane
+    // instead of a 64-bit address saves vector instructions in a loop that does G heads' work per
+    // load (Llama-3-8B GQA, batch 32, 8192 positions: 179 against 189 us per call on MI355X; with
+    // G = 1 the plain global loads are as fast or faster).  A sequence's cache slice,
+    // L_max x Hkv x D bf16, is checked at launch to fit the 31-bit offsets.
+    constexpr bool BUF = G > 1 && EPL == 8;
+    const int64_t seq0 = ((int64_t)b * a.L_max * a.Hkv + kvh) * D;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(a.kc + seq0), 0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(a.vc + seq0), 0, 0x7fffffff, 0x00020000);
 
     // NP positions per lane group per iteration, the same number of iterations for every lane
     // group (uniform control flow).  The K/V vectors of the next iteration are loaded before the
@@ -166,8 +176,16 @@ __global__ __launch_bounds__(256) void attn_decode_split(const AttnArgs a) {
         for (int p = 0; p < NP; ++p) {
             const int64_t j = jb + 16 * p;
             const int64_t jj = j < j1 ? j : j0;
-            kk[p] = ld_kv<EPL, true>(kbase + jj * rowstride);
-            vk[p] = ld_kv<EPL, true>(vbase + jj * rowstride);
+            if constexpr (BUF) {
+                const int off = (int)((li * EPL + jj * rowstride) * (int64_t)sizeof(bf16_t));
+                const u32x4 k4 = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, kAuxNonTemporal);
+                const u32x4 v4 = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, kAuxNonTemporal);
+                kk[p].w[0] = k4.x; kk[p].w[1] = k4.y; kk[p].w[2] = k4.z; kk[p].w[3] = k4.w;
+                vk[p].w[0] = v4.x; vk[p].w[1] = v4.y; vk[p].w[2] = v4.z; vk[p].w[3] = v4.w;
+            } else {
+                kk[p] = ld_kv<EPL, true>(kbase + jj * rowstride);
+                vk[p] = ld_kv<EPL, true>(vbase + jj * rowstride);
+            }
         }
     };
     const int niter = j1 > j0 ? (int)((j1 - j0 + 16 * NP - 1) / (16 * NP)) : 0;  // uniform
@@ -321,6 +339,10 @@ int attn_default_splits(int B, int Hkv, int64_t L_max) {
 }
 
 fsvd_status_t launch_attn_decode(const AttnArgs& a, hipStream_t st) {
+    // grouped 128-wide heads address a sequence's cache slice with 31-bit buffer offsets
+    if (a.D == 128 && a.Hq > a.Hkv && a.L_max * a.Hkv * a.D * (int64_t)sizeof(bf16_t) > 0x7fffffffLL)
+        return fail(FSVD_ERR_UNSUPPORTED, "decode attention: one sequence's cache (%lld bytes) exceeds 2 GiB",
+                    (long long)(a.L_max * a.Hkv * a.D * (int64_t)sizeof(bf16_t)));
     if (a.D == 128) return launch_decode_d<8>(a, st);
     if (a.D == 64) return launch_decode_d<4>(a, st);
     return fail(FSVD_ERR_UNSUPPORTED, "head dim %d not in {64,128}", a.D);
