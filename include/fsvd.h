@@ -318,10 +318,10 @@ fsvd_status_t fsvd_layernorm(const void* x, const void* residual, const void* ga
                              float eps, int64_t M, int64_t d, void* y, fsvd_dtype_t dtype, fsvd_stream_t stream);
 
 /* Measurement helper, not part of the layer path: reads the bytes of src (rounded down to a
- * multiple of 16) once from HBM with 16-byte non-temporal loads over the whole chip, so a timed
- * call gives the read-stream bandwidth this part sustains, the practical ceiling of the
- * HBM-bound decode kernels.  out [64] uint32 (device) receives an XOR of the data read (keeps
- * the loads live; its value is meaningless). */
+ * multiple of 16) once from HBM with 16-byte non-temporal loads over the whole chip, each
+ * workgroup streaming one contiguous slice, so a timed call gives the read-stream bandwidth this
+ * part sustains, the practical ceiling of the HBM-bound decode kernels.  out [64] uint32 (device)
+ * receives an XOR of the data read (keeps the loads live; its value is meaningless). */
 fsvd_status_t fsvd_read_stream_probe(const void* src, size_t bytes, void* out, fsvd_stream_t stream);
 
 /* cache_seqlens[b] += n for b < B (one tiny kernel; also the optional last node of a graph). */

@@ -492,3 +492,22 @@ def test_layernorm_residual(M, d, with_res, inplace):
     torch.cuda.synchronize()
     ref = O.layernorm(x + (r.astype(np.float64) if with_res else 0.0), g, b, 1e-12)
     assert rel(from_dev(y), ref) <= BF16_TOL
+
+
+# ----------------------------------------------------------------------------- measurement helper
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, (1 << 20) + 16 * 1001])
+def test_read_stream_probe_reads_every_vector_once(nbytes):
+    """The read-stream probe's 64 output words XOR to the XOR of every 32-bit word it read (the
+    buffer rounded down to 16 bytes), so a vector skipped or read twice by the slicing shows."""
+    say("read-stream probe", nbytes)
+    g = torch.Generator().manual_seed(nbytes)
+    words = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), generator=g, dtype=torch.int64).to(torch.int32)
+    src = words.cuda()
+    out = torch.zeros(64, dtype=torch.int32, device="cuda")
+    fsvd.fsvd_read_stream_probe(src, nbytes, out)
+    torch.cuda.synchronize()
+    n = (nbytes // 16) * 4
+    want = np.bitwise_xor.reduce(words[:n].numpy().view(np.uint32))
+    assert np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32)) == want
