@@ -35,6 +35,11 @@ constexpr float kNegBig = -1.0e30f;
 #ifndef FSVD_ATTN_NP
 #define FSVD_ATTN_NP 2      // decode: positions per lane group per iteration (16 * NP per workgroup)
 #endif
+#ifndef FSVD_ATTN_NP_GQA
+#define FSVD_ATTN_NP_GQA 4  // the same with 4 or more query heads per kv head (measured on MI355X,
+                            // GQA batch 32 x 8 kv heads, 8192 positions: 172.0 against 179.7 us per
+                            // call; with one head per kv head 4 is slower: batch 16 90.6 against 85.4)
+#endif
 #ifndef FSVD_ATTN_ROUND
 #define FSVD_ATTN_ROUND 16  // decode: partition lengths are multiples of this
 #endif
@@ -169,7 +174,7 @@ __global__ __launch_bounds__(256) void attn_decode_split(const AttnArgs a) {
     // current ones are used (two iterations in flight per wave); loads are unconditional, rows past
     // the partition re-read its first row, and such positions get zero weight.  The running max
     // is updated once per iteration for all NP positions, so the rescale of l and o is paid once.
-    constexpr int NP = FSVD_ATTN_NP;
+    constexpr int NP = G >= 4 ? FSVD_ATTN_NP_GQA : FSVD_ATTN_NP;
     KV<EPL> kv[NP], vv[NP];
     auto load = [&](int64_t jb, KV<EPL> (&kk)[NP], KV<EPL> (&vk)[NP]) {
 #pragma unroll
