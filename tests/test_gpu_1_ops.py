@@ -329,6 +329,7 @@ def _run_attn(q, kc, vc, seqlens, causal, L_max, Hkv):
     (1, 8, 1, 64, 4100, [4095], 1.0),            # GQA 8, D = 64, long
     (4, 32, 32, 128, 2304, [2048, 2100, 1, 2303], 8.0),
     (2, 16, 2, 128, 700, [5, 699], 8.0),         # GQA 8, D = 128 (65 KiB of LDS per workgroup)
+    (3, 8, 4, 128, 900, [100, 899, 0], 8.0),     # GQA 2, D = 128 (buffer loads, 2 positions per step)
     (4, 32, 32, 128, 16400, [16384, 16399, 9000, 0], 8.0),   # the 16,384-token decode horizon
 ])
 def test_attention_decode(B, Hq, Hkv, D, L_max, seqlens, qs):
