@@ -38,12 +38,12 @@ struct RowdotArgs {
     int ksplit;      // waves sharing one row group (split of the reduction): 1, 2, 4 or 8
     int waves;       // waves per workgroup: 4 or 8
     // matrix-core launches with few tiles: the reduction is also split over kpart workgroups
-    // (set by the planner when part is given); partial tiles go to part, and the last of a tile's
-    // kpart workgroups to finish sums them and runs the epilogue (counted in the workspace header
-    // behind err), or without that header a second kernel does.  nblk: tiles (workgroups per part).
+    // (set by the planner when part and err are given); partial tiles go to part, and the last of a
+    // tile's kpart workgroups to finish sums them and runs the epilogue, counted in the workspace
+    // header behind err.  nblk: tiles (workgroups per reduction part).
     int kpart, nblk;
     float* part;     // fp32 partial tiles, rowdot_part_bytes(M, dtype) bytes (NULL: no split)
-    unsigned* split_cnt;  // [nblk] counters in the workspace header (set by the launcher; NULL: second kernel)
+    unsigned* split_cnt;  // [nblk] counters in the workspace header (set by the launcher)
     const void* act; // [M, lda]
     int64_t lda;
     int M;

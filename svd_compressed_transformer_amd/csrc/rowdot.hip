@@ -396,9 +396,6 @@ typedef __bf16 bf16x8_m __attribute__((ext_vector_type(8)));
 typedef float f32x4_m __attribute__((ext_vector_type(4)));
 constexpr int kMfmaRows = 16;  // factor rows per wave tile
 constexpr int kAuxNonTemporal = 2;  // cache-policy operand of the direct-to-LDS load: nt
-#ifndef FSVD_RD_COUNTED_SPLIT
-#define FSVD_RD_COUNTED_SPLIT 1  // 0: split reductions always finish in the second kernel (for comparisons)
-#endif
 constexpr int kMfmaSteps = 8;  // 32-wide k steps whose loads one pass keeps in flight (16 activation rows)
 // Factor rows of a pass staged through a wave-private LDS buffer with row-contiguous loads (an
 // instruction reads 512 or 256 contiguous bytes of each of 2 or 4 rows) instead of loading the
@@ -426,9 +423,9 @@ __host__ __device__ inline int part_val_idx(int g, int h, int r, int m, int ns) 
 __host__ __device__ inline int part_ss_idx(int g, int m, int ngroups, int ns) { return ngroups * ns * kMfmaRows * 32 + g * 32 + m; }
 
 // Finishes tile blk of a split reduction: sums its kpart partial tiles in part order and runs the
-// epilogue of the unsplit kernel on them (same threads, same unit mapping).  COHERENT: the partials
-// were written in the same kernel by workgroups on any XCD, so they are read with agent-scope loads.
-template <int EPI, bool COHERENT>
+// epilogue of the unsplit kernel on them (same threads, same unit mapping).  The partials were
+// written in the same kernel by workgroups on any XCD, so they are read with agent-scope loads.
+template <int EPI>
 __device__ __forceinline__ void finish_split_tile(const RowdotArgs& a, int blk, int tid) {
     using T = bf16_t;
     const RowdotSeg sg = seg_of<EPI>(a, blk);
@@ -443,9 +440,7 @@ __device__ __forceinline__ void finish_split_tile(const RowdotArgs& a, int blk, 
     auto sum_parts = [&](int idx) -> float {
         float s = 0.f;
         for (int p = 0; p < a.kpart; ++p) {
-            const float* e = src + p * pstride + idx;
-            if constexpr (COHERENT) s += __hip_atomic_load(e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            else s += *e;
+            s += __hip_atomic_load(src + p * pstride + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         return s;
     };
@@ -666,7 +661,6 @@ __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
             // agent-scope store: written through to the level every XCD reads coherently
             __hip_atomic_store(dst + idx, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (a.split_cnt == nullptr) return;  // rowdot_part_reduce finishes the tile
         // The last of the tile's kpart workgroups to finish sums the partials.  Every thread waits
         // until its partial stores have completed before the barrier, and only then is the part
         // counted, so the workgroup that takes the last count reads every part back with agent-scope
@@ -681,7 +675,7 @@ __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
             is_last = last;
         }
         __syncthreads();
-        if (is_last) finish_split_tile<EPI, true>(a, bid, tid);
+        if (is_last) finish_split_tile<EPI>(a, bid, tid);
         return;
     }
     if constexpr (EPI == EPI_LINEAR) {
@@ -689,12 +683,6 @@ __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
     }
     rowdot_epilogue<T, EPI>(a, sg, (bid - sg.blk_begin) * sg.units_per_blk, ngroups, upw, kMfmaRows / 2, n_units, tid,
                             64 * a.waves, val, ssq);
-}
-
-// Second kernel of a split reduction (no counters): workgroup blk finishes tile blk.
-template <int EPI>
-__global__ __launch_bounds__(512) void rowdot_part_reduce(const RowdotArgs a) {
-    finish_split_tile<EPI, false>(a, (int)blockIdx.x, (int)threadIdx.x);
 }
 
 template <typename T, int EPI>
@@ -805,9 +793,7 @@ fsvd_status_t launch_mfma(const RowdotArgs& a, int grid, hipStream_t st) {
         const bool db = (steps + mfma_pass_steps<2>() - 1) / mfma_pass_steps<2>() >= 3;
         s = db ? launch_mfma_t<2, EPI, true>(a, grid, st) : launch_mfma_t<2, EPI, false>(a, grid, st);
     }
-    if (s != FSVD_OK || a.kpart <= 1 || a.split_cnt) return s;
-    rowdot_part_reduce<EPI><<<a.nblk, 64 * a.waves, 0, st>>>(a);
-    return check_launch("rowdot_part_reduce");
+    return s;
 }
 
 }  // namespace
@@ -824,12 +810,17 @@ int rowdot_plan(RowdotArgs& a, int epi, fsvd_dtype_t dtype) {
 fsvd_status_t launch_rowdot(const RowdotArgs& a, int epi, fsvd_dtype_t dtype, hipStream_t st) {
     RowdotArgs c = a;
     if (c.M < 1 || c.M > 32) return fail(FSVD_ERR_UNSUPPORTED, "row-dot path supports 1..32 activation rows, got %d", c.M);
-    const int grid = rowdot_plan(c, epi, dtype);
+    // A split reduction counts its finished parts in the workspace header (err is its first word);
+    // without a header the reduction is not split.
+    if (c.err == nullptr) c.part = nullptr;
+    int grid = rowdot_plan(c, epi, dtype);
+    if (c.kpart > 1 && c.nblk > kWsSplitCounters) {  // cannot happen (a split launch has <= 128 tiles)
+        c.part = nullptr;
+        grid = rowdot_plan(c, epi, dtype);
+    }
     if (grid <= 0) return FSVD_OK;
-    // a split reduction counts its finished parts in the workspace header (err is its first word)
-    c.split_cnt = (FSVD_RD_COUNTED_SPLIT && c.kpart > 1 && c.err != nullptr && c.nblk <= kWsSplitCounters)
-                      ? reinterpret_cast<unsigned*>(reinterpret_cast<char*>(c.err) + kWsSplitCounterOff)
-                      : nullptr;
+    c.split_cnt = c.kpart > 1 ? reinterpret_cast<unsigned*>(reinterpret_cast<char*>(c.err) + kWsSplitCounterOff)
+                              : nullptr;
     if (dtype == FSVD_F32) {
         switch (epi) {
             case EPI_Z: return launch_b<float, EPI_Z>(c, grid, st);
