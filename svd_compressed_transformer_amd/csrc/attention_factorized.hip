@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kFThreads) void attn_factorized_mfma(const FactAttn
     // still being filled and keeps the chunk prefetch in flight across the attention step.
     extern __shared__ u32x4 CH[];                      // NB chunk buffers
     __shared__ u32x4 Ks[BKV * KCH];                    // key tile, permuted head order, swizzled
-    __shared__ uint2 Vts[D * 16];                      // value tile, transposed
+    __shared__ u32x4 Vt[D * 8];                        // value tile, transposed (vts_slot)
     bf16_t* Ks16 = reinterpret_cast<bf16_t*>(Ks);
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -406,11 +406,11 @@ __global__ __launch_bounds__(kFThreads) void attn_factorized_mfma(const FactAttn
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const int d = (dp + hh * NDP) * 16 + li, kc = (kg * KB + kb) * 4 + lg;
-                    Vts[d * 16 + (kc ^ (d & 15))] = pack4(acc[kb][hh]);
+                    reinterpret_cast<uint2*>(Vt)[vts_slot(d, kc)] = pack4(acc[kb][hh]);
                 }
         }
         lds_barrier();
-        attn_tile<D, QW>(Ks, Vts, qf, j0, n_lane, n_min_w, sc, m, l, o, li, lg);
+        attn_tile<D, QW>(Ks, Vt, qf, j0, n_lane, n_min_w, sc, m, l, o, li, lg);
     }
 
 #pragma unroll

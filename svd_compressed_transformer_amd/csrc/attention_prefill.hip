@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma(const AttnArgs a) {
     constexpr int VG = 16 * (D / 8);       // V staging groups of 4 keys x 8 dims
     constexpr int VLD = (VG + 255) / 256;  // groups per thread
     __shared__ u32x4 Ks[BKV * KCH];
-    __shared__ uint2 Vts[D * 16];
+    __shared__ u32x4 Vt[D * 8];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma(const AttnArgs a) {
                 const uint32_t v0 = (vreg[i][0][w] >> sh) & 0xffffu, v1 = (vreg[i][1][w] >> sh) & 0xffffu;
                 const uint32_t v2 = (vreg[i][2][w] >> sh) & 0xffffu, v3 = (vreg[i][3][w] >> sh) & 0xffffu;
                 const int d = dg * 8 + e;
-                Vts[d * 16 + (kc ^ (d & 15))] = uint2{v0 | (v1 << 16), v2 | (v3 << 16)};
+                reinterpret_cast<uint2*>(Vt)[vts_slot(d, kc)] = uint2{v0 | (v1 << 16), v2 | (v3 << 16)};
             }
         }
     };
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma(const AttnArgs a) {
         __syncthreads();
         if (j0 + BKV < kend) prefetch(j0 + BKV);
 
-        attn_tile<D, QW>(Ks, Vts, qf, (int)j0, n_lane, (int)n_min, sc, m, l, o, li, lg);
+        attn_tile<D, QW>(Ks, Vt, qf, (int)j0, n_lane, (int)n_min, sc, m, l, o, li, lg);
     }
 
 #pragma unroll

@@ -26,8 +26,11 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
     __bf16 h = static_cast<__bf16>(f);
     return __builtin_bit_cast(bf16_t, h);
 }
+// two values in one v_cvt_pk_bf16_f32 (converted one at a time, the halves take a shift and an or
+// more); the same rounding as f2bf
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+    typedef float f32x2_c __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_c{lo, hi}, bf16x2_v));
 }
 
 // a.x*b.x + a.y*b.y + c on two packed bf16 pairs, fp32 accumulate
