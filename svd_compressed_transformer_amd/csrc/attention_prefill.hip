@@ -82,6 +82,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma(const AttnArgs a) {
     const bf16_t* kb0 = a.kc + ((int64_t)b * a.L_max * a.Hkv + g) * D;
     const bf16_t* vb0 = a.vc + ((int64_t)b * a.L_max * a.Hkv + g) * D;
 
+    // Rows past kend (the last tile's tail) re-read row kend - 1, a written cache row: their keys
+    // are masked (a select, so any finite K will do) and their values get probability 0 (finite V
+    // keeps 0 * v at 0).  Unconditional loads keep the prefetch free of branches.
     u32x4 kreg[KLD];
     u32x4 vreg[VLD][4];
     auto prefetch = [&](int64_t j0) {
@@ -89,18 +92,18 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma(const AttnArgs a) {
         for (int i = 0; i < KLD; ++i) {
             const int q = tid + 256 * i;
             const int key = q / KCH, ch = q % KCH;
-            const int64_t j = j0 + key;
-            kreg[i] = j < kend ? *reinterpret_cast<const u32x4*>(kb0 + j * rowstride + ch * 8) : u32x4{0u, 0u, 0u, 0u};
+            const int64_t j = min(j0 + key, kend - 1);
+            kreg[i] = *reinterpret_cast<const u32x4*>(kb0 + j * rowstride + ch * 8);
         }
 #pragma unroll
         for (int i = 0; i < VLD; ++i) {
             const int gi = tid + 256 * i;
+            if (gi >= VG) continue;  // wave-uniform (D = 64: the upper half of the workgroup)
             const int kc = gi & 15, dg = gi >> 4;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t j = j0 + kc * 4 + r;
-                vreg[i][r] = (gi < VG && j < kend) ? *reinterpret_cast<const u32x4*>(vb0 + j * rowstride + dg * 8)
-                                                   : u32x4{0u, 0u, 0u, 0u};
+                const int64_t j = min(j0 + kc * 4 + r, kend - 1);
+                vreg[i][r] = *reinterpret_cast<const u32x4*>(vb0 + j * rowstride + dg * 8);
             }
         }
     };

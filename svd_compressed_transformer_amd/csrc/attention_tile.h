@@ -51,11 +51,13 @@ __device__ __forceinline__ void attn_tile_m(const u32x4* Ks, const u32x4* Vt, co
             for (int q = 0; q < QW; ++q) s[q][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[q][t], s[q][kb], 0, 0, 0);
         }
     }
-    // Online softmax in the log2 domain.  The tile max is taken over the raw scores (sc > 0, so
-    // it is the max of the scaled ones) and the scale enters the exponent's fma.  The running max
-    // m is raised, and l and o rescaled, only when some query of the wave sees a tile max more
-    // than kStaleLog2 above it: until then p = 2^(s*sc - m) <= 2^kStaleLog2 with the stale m,
-    // which changes no result (m cancels in o / l) and skips the rescale on most tiles.
+    // Online softmax in the log2 domain.  Maxima are taken over the raw scores (sc > 0, so they
+    // are the maxima of the scaled ones) and the scale enters the exponent's fma.  The running max
+    // m of a query (the same in its 4 lanes) is raised, and l and o rescaled, only when some lane
+    // of the wave holds a score more than kStaleLog2 above it; only then are the query's 4 lanes
+    // combined (two cross-lane exchanges).  Until then p = 2^(s*sc - m) <= 2^kStaleLog2 with the
+    // stale m, which changes no result (m cancels in o / l) and skips the rescale and the
+    // exchanges on most tiles.
     constexpr float kStaleLog2 = 8.0f;
     bf16x8_v pf[QW][2];
 #pragma unroll
@@ -72,11 +74,10 @@ __device__ __forceinline__ void attn_tile_m(const u32x4* Ks, const u32x4* Vt, co
                 }
                 tmax = fmaxf(tmax, v);
             }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float tm = tmax * sc;
-        if (__builtin_amdgcn_ballot_w64(tm > m[q] + kStaleLog2) != 0) {  // wave-uniform
-            const float mn = fmaxf(m[q], tm);
+        if (__builtin_amdgcn_ballot_w64(tmax * sc > m[q] + kStaleLog2) != 0) {  // wave-uniform
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const float mn = fmaxf(m[q], tmax * sc);
             const float alpha = __builtin_amdgcn_exp2f(m[q] - mn);
             l[q] *= alpha;
 #pragma unroll
