@@ -420,6 +420,35 @@ def test_attention_multi_token(B, Sq, Hq, Hkv, D, L_max, sl, causal):
     assert rel(o, O.attention(q, kc, vc, sl, causal=causal)) <= BF16_TOL
 
 
+# Scores that climb or fall steeply along the cache.  The multi-token kernel raises a query's
+# running max only when one of its scores passes it by more than 8 in the log2 domain (the
+# probabilities use the stale max until then).  A climbing ramp, about 12 log2 units per 64-key
+# tile, takes that path, which also combines the query's lanes, on every tile; a falling ramp keeps
+# the first tile's max, so the later tiles' probabilities fall far below 1 and then to 0.  The last
+# case has 1024 blocks of 128 queries: two query sets per wave.
+@pytest.mark.parametrize("slope", [1.0, -1.0])
+@pytest.mark.parametrize("B,Sq,Hq,Hkv,D,L_max,sl,causal", [
+    (2, 200, 8, 2, 128, 320, [0, 64], True),
+    (1, 150, 4, 4, 64, 256, [90], False),
+    (2, 256, 256, 32, 64, 320, [0, 60], True),
+])
+def test_attention_multi_token_score_ramps(B, Sq, Hq, Hkv, D, L_max, sl, causal, slope):
+    say("attn Sq>1 score ramp", B, Sq, Hq, Hkv, D, causal, slope)
+    q, kc, vc, _ = I.make_attention_case(B, Sq, Hq, Hkv, D, L_max, sl, seed=9)
+    rng = np.random.default_rng(19)
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    c = 4.0                                      # q's component along u
+    per_key = 12.0 / np.log2(np.e) / 64.0        # natural-log score step per key
+    alpha = per_key * np.sqrt(D) / c             # k's growth along u per key
+    q = I.round_bf16(q + c * u)
+    j = np.arange(L_max, dtype=np.float64)[None, :, None, None]
+    kc = I.round_bf16(kc + slope * alpha * (j - L_max / 2) * u)
+    o, ws = _run_attn(q, kc, vc, sl, causal, L_max, Hkv)
+    assert fsvd.fsvd_poll_device_error(ws) == 0
+    assert rel(o, O.attention(q, kc, vc, sl, causal=causal)) <= BF16_TOL
+
+
 def test_attention_overflow_flag():
     B, Hq, Hkv, D, L_max = 1, 2, 2, 64, 32
     q, kc, vc, _ = I.make_attention_case(B, 1, Hq, Hkv, D, L_max, [31])
