@@ -22,6 +22,9 @@
 //   kernels9: the layer-step with the attention partitions merged inside the attention kernel (the
 //             2.2 MB merge phase gone, the attention phase at 512 workgroups); then the same 9
 //             phases with every grid at 512, 1024 and 2048 workgroups.
+//   kernels9_mall: the 9 phases at the decode grids, each kernel reading 25 / 50 / 100% of the next
+//             phase's bytes with ordinary loads after its own stream (into the Infinity Cache).
+// A first argument n runs the variants from n on.
 //
 // Every activation word encodes (layer-step, phase, slot); each reader counts the words it does not
 // find as expected, which the run reports (a stale read would show there).  Every spin is bounded:
@@ -31,6 +34,7 @@
 #include <cstdint>
 #include <vector>
 #include <algorithm>
+#include <cstdlib>
 #define CK(x) do { hipError_t e_ = (x); if (e_ != hipSuccess) { printf("%s:%d %s\n", __FILE__, __LINE__, hipGetErrorString(e_)); return 1; } } while (0)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -103,6 +107,38 @@ __global__ __launch_bounds__(256) void phase_kernel(const u32x4* __restrict__ w,
     }
     if (acc == 0x12345678u) sink[blockIdx.x & 63] = acc;  // keeps the loads live
     write_act<false>(act, step, p);
+}
+
+// phase_kernel, then a share of the first pn16 vectors of the NEXT phase's bytes read with ordinary
+// (allocating) loads after this phase's own stream: the memory-side Infinity Cache holds them when
+// the next kernel starts, and this kernel's tail keeps HBM busy.
+__global__ __launch_bounds__(256) void phase_mall_kernel(const u32x4* __restrict__ w, long n16, uint32_t* act, int p,
+                                                         uint32_t step, unsigned* bad, uint32_t* sink, int skip,
+                                                         const u32x4* __restrict__ pw, long pn16) {
+    read_act<false>(act, step, p - skip, bad);
+    const long stride = (long)gridDim.x * blockDim.x;
+    long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4 a = __builtin_nontemporal_load(w + i), b = __builtin_nontemporal_load(w + i + stride);
+        const u32x4 c = __builtin_nontemporal_load(w + i + 2 * stride), d = __builtin_nontemporal_load(w + i + 3 * stride);
+        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 a = __builtin_nontemporal_load(w + i);
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    write_act<false>(act, step, p);
+    i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < pn16; i += 4 * stride) {
+        const u32x4 a = pw[i], b = pw[i + stride], c = pw[i + 2 * stride], d = pw[i + 3 * stride];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    }
+    for (; i < pn16; i += stride) {
+        const u32x4 a = pw[i];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    if (acc == 0x12345678u) sink[blockIdx.x & 63] = acc;  // keeps the loads live
 }
 
 // two-level barrier number k (k = 1, 2, ...): XCD counter, the last arriver of an XCD bumps the
@@ -249,7 +285,8 @@ __global__ __launch_bounds__(256, 1) void persist_lds_kernel(Phases ph, uint32_t
     if (acc == 0x12345678u) sink[blockIdx.x & 63] = acc;
 }
 
-int main() {
+int main(int argc, char** argv) {
+    const int first = argc > 1 ? atoi(argv[1]) : 0;  // first variant to run
     int dev = 0, cus = 0;
     CK(hipGetDevice(&dev));
     CK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
@@ -286,8 +323,9 @@ int main() {
     // each copy's graph is captured with a fixed step and the activation check tolerates reuse by
     // writing before reading within the same graph (phase 0 reads nothing)
     CK(hipFuncSetAttribute((const void*)persist_lds_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, LDSV * 16));
-    constexpr int NV = 10;
-    for (int variant = 0; variant < NV; ++variant) {
+    constexpr int NV = 13;
+    constexpr double MALL_F[3] = {0.25, 0.5, 1.0};  // variants 10-12: fraction of the next phase prefetched
+    for (int variant = first; variant < NV; ++variant) {
         std::vector<float> v;
         for (int rep = 0; rep < 5; ++rep) {
             CK(hipMemsetAsync(xcnt, 0, 8 * 32 * 4, st)); CK(hipMemsetAsync(gcnt, 0, 4, st));
@@ -305,6 +343,16 @@ int main() {
                             continue;
                         }
                         if (GRID9[p] == 0) { skip = 1; continue; }
+                        if (variant >= 10) {  // next phase: p + 1 (past the skipped merge), or the next copy's phase 0
+                            int q = p + 1;
+                            if (q < P && GRID9[q] == 0) ++q;
+                            const u32x4* pw = q < P ? ph[l].w[q] : ph[(l + 1) % NL].w[0];
+                            const long pn = (long)(MALL_F[variant - 10] * (double)(q < P ? n16[q] : n16[0]));
+                            phase_mall_kernel<<<GRID9[p], 256, 0, st>>>(ph[l].w[p], n16[p], act, p, (uint32_t)l, bad,
+                                                                        sink, skip, pw, pn);
+                            skip = 0;
+                            continue;
+                        }
                         const int grid = variant == 6 ? GRID9[p] : variant == 7 ? 512 : variant == 8 ? 1024 : 2048;
                         phase_kernel<<<grid, 256, 0, st>>>(ph[l].w[p], n16[p], act, p, (uint32_t)l, bad, sink, skip);
                         skip = 0;
@@ -355,7 +403,8 @@ int main() {
         std::sort(v.begin(), v.end());
         const double us = v[2] * 1e3 / steps;
         const char* name[NV] = {"kernels", "persist", "prefetch", "persist_depth16", "prefetch_depth16", "lds_prefetch",
-                                "kernels9", "kernels9_grid512", "kernels9_grid1024", "kernels9_grid2048"};
+                                "kernels9", "kernels9_grid512", "kernels9_grid1024", "kernels9_grid2048",
+                                "kernels9_mall25", "kernels9_mall50", "kernels9_mall100"};
         const double vb = variant >= 6 ? bytes - (double)n16[3] * 16 : bytes;  // the 9 phases skip the merge's bytes
         printf("{\"variant\": \"%s\", \"us_per_layer_step\": %.2f, \"gbs\": %.1f, \"of_8tbs\": %.3f}\n", name[variant], us,
                vb / (us * 1e-6) / 1e9, vb / (us * 1e-6) / 8e12);
