@@ -73,7 +73,7 @@ extern "C" {
 
 typedef struct ihipStream_t* fsvd_stream_t; /* a hipStream_t */
 
-#define FSVD_ABI_VERSION 7
+#define FSVD_ABI_VERSION 8
 
 typedef enum {
     FSVD_OK = 0,
@@ -316,6 +316,18 @@ fsvd_status_t fsvd_swift_factors(const void* Wt, int64_t d_out, int64_t d_in, co
  * ------------------------------------------------------------------------------------------ */
 fsvd_status_t fsvd_layernorm(const void* x, const void* residual, const void* gamma, const void* beta,
                              float eps, int64_t M, int64_t d, void* y, fsvd_dtype_t dtype, fsvd_stream_t stream);
+
+/* Comparator, not part of the layer path: the dense projection the factors replace, through the
+ * same kernels as the low-rank linear's second phase ("FlashSVD v1.5" explainer, Results: the
+ * low-rank path is measured against the model's dense weights).
+ *   y[m, :] = residual[m, :] + bias + x[m, :] . W^T
+ * x [M, K] (ldx), W [N, K] (ldw), bias [N] or NULL, residual [M, N] (ldr) or NULL (may alias y),
+ * y [M, N] (ldy).  M <= 32 runs the row-dot kernels (bf16 launches of 5..32 rows on the matrix
+ * cores, the reduction not split across workgroups); larger M the bf16 MFMA GEMM (bf16 only).
+ * No workspace; argument errors are returned before anything is launched. */
+fsvd_status_t fsvd_dense_linear(const void* x, int64_t M, int64_t K, int64_t ldx, const void* W, int64_t N,
+                                int64_t ldw, const void* bias, const void* residual, int64_t ldr, void* y,
+                                int64_t ldy, fsvd_dtype_t dtype, fsvd_stream_t stream);
 
 /* Measurement helper, not part of the layer path: reads the bytes of src (rounded down to a
  * multiple of 16) once from HBM with 16-byte non-temporal loads over the whole chip, each

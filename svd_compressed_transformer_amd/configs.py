@@ -28,6 +28,11 @@ One JSON line per measurement on stdout:
   materialised q, K, V: BERT-Base encoder (8 x 512, 12 x 64, rank 384, no mask) and a causal
   Llama-7B prefill of one 2048-token sequence (32 x 128, rank 1638 stored as 1664, RoPE); the bytes of q, k, v the
   factorised form never writes.
+- dense_vs_lowrank_llama7b_m{1,4,8192}: the seven projections of a Llama-7B-shaped layer (q, k, v,
+  o: 4096 -> 4096; gate, up: 4096 -> 11008; down: 11008 -> 4096) as plain linears over 1, 4 or
+  8192 token rows, each once with the dense weight W = U.V (fsvd_dense_linear: one kernel) and once
+  with the rank-1638 factors (fsvd_lowrank_linear: two kernels), through the same kernels; no
+  norm, activation, RoPE or cache work on either side; 4 weight copies rotated.
 - attn_lowrank_history_llama7b_b{1,4}: the decode attention of a Llama-7B-shaped layer over a
   2048-token history, from the dense KV cache against the layout the dense cache replaces
   (rank-1638 rows z_k, z_v cached per token, K and V rebuilt from them every step, then the same
@@ -295,6 +300,67 @@ def run_decode_stack(name, cfg, ranks, B, history, layers, dev, stream):
     return res
 
 
+# ----------------------------------------------------------------------------- dense weights vs factors
+
+
+def run_dense_vs_lowrank(M, dev, stream, copies=4):
+    """The layer's seven projections as plain linears, dense W against the rank-r factors."""
+    c = I.CFG2
+    d, dff = c.d, c.d_ff
+    shapes = {"q": (d, d), "k": (d, d), "v": (d, d), "o": (d, d), "gate": (d, dff), "up": (d, dff), "down": (dff, d)}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    bf = fsvd.FSVD_BF16
+    res = {"config": f"dense_vs_lowrank_llama7b_m{M}", "rows": M, "projections": {}}
+    tot_d = tot_l = by_d = by_l = fl_d = fl_l = 0.0
+    for name, (K, N) in shapes.items():
+        r = c.ranks[name]
+        rs = (r + 31) // 32 * 32  # stored rank, as the layer stores it
+        x = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        fac, dense = [], []
+        for _ in range(copies):
+            Ut, Vt = _factor(gen, K, N, r, dev)
+            Ut = torch.cat([Ut, torch.zeros((rs - r, K), dtype=Ut.dtype, device=dev)]) if rs > r else Ut
+            Vt = pad_cols_dev(Vt, rs)
+            fac.append((Ut, Vt))
+            dense.append((Vt.float() @ Ut.float()).to(torch.bfloat16))  # W [N, K] = (U V)^T
+        ws = fsvd.workspace(fsvd.fsvd_lowrank_linear_ws(M, K, rs, N, bf), device=dev)
+        it = {"d": 0, "l": 0}
+
+        def dense_call():
+            W = dense[it["d"] % copies]
+            it["d"] += 1
+            fsvd.fsvd_dense_linear(x, M, K, K, W, N, K, None, None, N, y, N, bf, stream)
+
+        def lowrank_call():
+            Ut, Vt = fac[it["l"] % copies]
+            it["l"] += 1
+            fsvd.fsvd_lowrank_linear(x, M, K, K, Ut, rs, K, Vt, N, rs, None, None, N, y, N, bf, ws, ws.numel(),
+                                     stream)
+
+        t_d = timed_median(dense_call, stream, min_ms=10.0)
+        t_l = timed_median(lowrank_call, stream, min_ms=10.0)
+        b_d = 2 * (N * K + M * K + M * N)
+        b_l = 2 * (r * (K + N) + M * K + M * N)
+        f_d, f_l = 2.0 * M * K * N, 2.0 * M * r * (K + N)
+        res["projections"][name] = {"K": K, "N": N, "rank": r, "dense_us": round(t_d * 1e3, 2),
+                                    "lowrank_us": round(t_l * 1e3, 2)}
+        tot_d += t_d; tot_l += t_l; by_d += b_d; by_l += b_l; fl_d += f_d; fl_l += f_l
+        del fac, dense, ws
+        torch.cuda.empty_cache()
+    res.update({"dense_us": round(tot_d * 1e3, 2), "lowrank_us": round(tot_l * 1e3, 2),
+                "lowrank_speedup": round(tot_d / tot_l, 3), "dense_bytes": int(by_d), "lowrank_bytes": int(by_l),
+                "dense_flops": int(fl_d), "lowrank_flops": int(fl_l)})
+    if M <= 32:
+        res["dense_frac_of_8tbs"] = round(by_d / (tot_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        res["lowrank_frac_of_8tbs"] = round(by_l / (tot_l * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    else:
+        res["dense_mfma_frac"] = round(fl_d / (tot_d * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+        res["lowrank_mfma_frac"] = round(fl_l / (tot_l * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+    return res
+
+
 # ----------------------------------------------------------------------------- dense KV vs low-rank history
 
 
@@ -450,6 +516,8 @@ def main():
     runs.append(("attn_factorized_llama7b_s2048",
                  lambda: run_attn_factorized("attn_factorized_llama7b_s2048", 1, 2048, 32, 128, 1664, 1e4, True, dev,
                                              stream)))
+    for M in (1, 4, 8192):
+        runs.append((f"dense_vs_lowrank_llama7b_m{M}", lambda M=M: run_dense_vs_lowrank(M, dev, stream)))
     for B in (1, 4):
         runs.append((f"attn_lowrank_history_llama7b_b{B}", lambda B=B: run_attn_history(B, 2048, dev, stream)))
     only = set(filter(None, args.only.split(",")))

@@ -718,6 +718,34 @@ fsvd_status_t fsvd_lowrank_linear(const void* x, int64_t M, int64_t K, int64_t l
     return run_linear(x, M, K, ldx, Ut, r, ldu, Vt, N, ldv, bias, residual, ldr, y, ldy, dtype, ws, (hipStream_t)stream);
 }
 
+fsvd_status_t fsvd_dense_linear(const void* x, int64_t M, int64_t K, int64_t ldx, const void* W, int64_t N,
+                                int64_t ldw, const void* bias, const void* residual, int64_t ldr, void* y,
+                                int64_t ldy, fsvd_dtype_t dtype, fsvd_stream_t stream) {
+    TRY(need_dtype(dtype, true));
+    TRY(need_dim(M, "M")); TRY(need_dim(K, "K")); TRY(need_dim(N, "N"));
+    TRY(need_vec(K, dtype, "K")); TRY(need_vec(N, dtype, "N"));
+    TRY(need_ptr(x, "x")); TRY(need_ptr(W, "W")); TRY(need_ptr(y, "y"));
+    TRY(opt_ptr(bias, "bias")); TRY(opt_ptr(residual, "residual"));
+    TRY(need_ld(ldx, K, dtype, "ldx")); TRY(need_ld(ldw, K, dtype, "ldw")); TRY(need_ld(ldy, N, dtype, "ldy"));
+    if (residual) TRY(need_ld(ldr, N, dtype, "ldr"));
+    const hipStream_t st = (hipStream_t)stream;
+    if (M <= kRowdotMaxM) {
+        RowdotArgs b{};  // no error word: the reduction is not split
+        b.nseg = 1;
+        b.act = x; b.lda = ldx; b.M = (int)M;
+        b.seg[0].W = W; b.seg[0].ldw = ldw; b.seg[0].N = (int)N; b.seg[0].K = (int)K; b.seg[0].out = y;
+        b.seg[0].ldo = ldy;
+        b.bias = bias; b.residual = residual; b.ldr = ldr;
+        return launch_rowdot(b, EPI_LINEAR, dtype, st);
+    }
+    if (dtype != FSVD_BF16) return fail(FSVD_ERR_UNSUPPORTED, "the MFMA path (M > %d) is bf16 only", kRowdotMaxM);
+    GemmArgs h{};
+    h.A = (const bf16_t*)x; h.lda = ldx; h.Bm = (const bf16_t*)W; h.ldb = ldw;
+    h.M = (int)M; h.N = (int)N; h.K = (int)K; h.C = (bf16_t*)y; h.ldc = ldy;
+    h.bias = (const bf16_t*)bias; h.residual = (const bf16_t*)residual; h.ldr = ldr;
+    return launch_gemm(h, GEPI_LINEAR, st);
+}
+
 fsvd_status_t fsvd_lowrank_linear_noalloc(const void* x, int64_t M, int64_t K, int64_t ldx, const void* Ut, int64_t r,
                                           int64_t ldu, const void* Vt, int64_t N, int64_t ldv, const void* bias,
                                           const void* residual, int64_t ldr, void* y, int64_t ldy, fsvd_dtype_t dtype,

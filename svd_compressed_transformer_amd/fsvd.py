@@ -73,6 +73,8 @@ _SIGS = {
     "fsvd_swift_factors": (C.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "fsvd_layernorm": (C.c_int, [_vp, _vp, _vp, _vp, _f32, _i64, _i64, _vp, C.c_int, _vp]),
     "fsvd_seqlens_advance": (C.c_int, [_vp, _i64, _i32, _vp]),
+    "fsvd_dense_linear": (C.c_int, [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i64, C.c_int,
+                                    _vp]),
     "fsvd_read_stream_probe": (C.c_int, [_vp, _sz, _vp, _vp]),
     "fsvd_decoder_layer_ws": (_sz, [C.POINTER(DecoderLayerDesc)]),
     "fsvd_decoder_layer_run": (C.c_int, [C.POINTER(DecoderLayerDesc), _vp]),
@@ -261,6 +263,12 @@ def fsvd_swift_factors(Wt, d_out, d_in, VkT, k, Ut, Vt, ws, ws_bytes, stream=Non
 
 def fsvd_layernorm(x, residual, gamma, beta, eps, M, d, y, dtype, stream=None):
     _check(lib().fsvd_layernorm(_p(x), _p(residual), _p(gamma), _p(beta), eps, M, d, _p(y), dtype, _s(stream)))
+
+
+def fsvd_dense_linear(x, M, K, ldx, W, N, ldw, bias, residual, ldr, y, ldy, dtype, stream=None):
+    """Comparator: y = residual + bias + x . W^T through the low-rank linear's second-phase kernels."""
+    _check(lib().fsvd_dense_linear(_p(x), M, K, ldx, _p(W), N, ldw, _p(bias), _p(residual), ldr, _p(y), ldy, dtype,
+                                   _s(stream)))
 
 
 def fsvd_read_stream_probe(src, nbytes, out, stream=None):

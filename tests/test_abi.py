@@ -136,6 +136,14 @@ def test_validation_errors_return_before_launch(L, monkeypatch):
     assert s == fsvd.FSVD_ERR_CAPTURE
     s, _ = _status(lambda: fsvd.fsvd_graph_destroy(0x1234))
     assert s == fsvd.FSVD_ERR_CAPTURE
+    # dense-weight comparator: NULL weight, short leading dimension, fp32 beyond the row-dot sizes
+    s, msg = _status(lambda: fsvd.fsvd_dense_linear(0x1000, 1, 8, 8, None, 8, 8, None, None, 8, 0x2000, 8, bf))
+    assert s == fsvd.FSVD_ERR_INVALID_ARG and "NULL" in msg
+    s, msg = _status(lambda: fsvd.fsvd_dense_linear(0x1000, 1, 16, 16, 0x2000, 8, 8, None, None, 8, 0x3000, 8, bf))
+    assert s == fsvd.FSVD_ERR_INVALID_ARG and "ldw" in msg
+    s, _ = _status(lambda: fsvd.fsvd_dense_linear(0x1000, 64, 8, 8, 0x2000, 8, 8, None, None, 8, 0x3000, 8,
+                                                  fsvd.FSVD_F32))
+    assert s == fsvd.FSVD_ERR_UNSUPPORTED
     # prepack with inconsistent extents
     s, _ = _status(lambda: fsvd.fsvd_prepack(0x1000, 8, 8, [(0x1000, 4, 16, 16, 4)], bf))
     assert s == fsvd.FSVD_ERR_INVALID_ARG

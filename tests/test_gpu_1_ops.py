@@ -165,6 +165,28 @@ def test_linear_deterministic(M):
     assert np.array_equal(y1, y2)
 
 
+@pytest.mark.parametrize("dtype,M,K,N,extras", [("bf16", 1, 4096, 4096, False), ("bf16", 4, 1000, 1032, True),
+                                                 ("bf16", 20, 768, 392, True), ("f32", 4, 640, 392, True),
+                                                 ("bf16", 300, 1000, 1032, True), ("bf16", 2100, 4096, 1024, False)])
+def test_dense_linear_comparator(dtype, M, K, N, extras):
+    """The dense-weight comparator y = x . W^T (+ bias + residual): the oracle's low-rank linear at
+    full rank with W as the first factor and the identity as the second is that same map."""
+    say("dense linear", dtype, M, K, N, "bias+residual" if extras else "")
+    rng = np.random.default_rng(M + N)
+    x = I.round_to(rng.standard_normal((M, K)), dtype)
+    W = I.round_to(rng.standard_normal((N, K)) / np.sqrt(K), dtype)
+    b = I.round_to(rng.standard_normal(N), dtype) if extras else None
+    res = I.round_to(rng.standard_normal((M, N)), dtype) if extras else None
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    fdt = fsvd.FSVD_F32 if dtype == "f32" else fsvd.FSVD_BF16
+    y = torch.empty((M, N), dtype=tdt, device="cuda")
+    fsvd.fsvd_dense_linear(to_dev(x, tdt), M, K, K, to_dev(W, tdt), N, K, to_dev(b, tdt) if extras else None,
+                           to_dev(res, tdt) if extras else None, N, y, N, fdt)
+    torch.cuda.synchronize()
+    ref = O.lowrank_linear(x, W, np.eye(N), bias=b, residual=res)
+    assert rel(from_dev(y), ref) <= (BF16_TOL if dtype == "bf16" else F32_TOL)
+
+
 # ----------------------------------------------------------------------------- Q/K/V with KV append (a5)
 
 
