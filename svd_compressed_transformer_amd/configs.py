@@ -33,6 +33,8 @@ One JSON line per measurement on stdout:
   8192 token rows, each once with the dense weight W = U.V (fsvd_dense_linear: one kernel) and once
   with the rank-1638 factors (fsvd_lowrank_linear: two kernels), through the same kernels; no
   norm, activation, RoPE or cache work on either side; 4 weight copies rotated.
+- dense_vs_lowrank_ratios_llama7b_m{1,4,8192}: the same at rank ratios 0.1-0.6 of min(dims) on every
+  projection: the low-rank speedup over the dense weights against the compression ratio.
 - attn_lowrank_history_llama7b_b{1,4}: the decode attention of a Llama-7B-shaped layer over a
   2048-token history, from the dense KV cache against the layout the dense cache replaces
   (rank-1638 rows z_k, z_v cached per token, K and V rebuilt from them every step, then the same
@@ -303,18 +305,22 @@ def run_decode_stack(name, cfg, ranks, B, history, layers, dev, stream):
 # ----------------------------------------------------------------------------- dense weights vs factors
 
 
-def run_dense_vs_lowrank(M, dev, stream, copies=4):
-    """The layer's seven projections as plain linears, dense W against the rank-r factors."""
+def run_dense_vs_lowrank(M, dev, stream, copies=4, ratio=None, dense_us=None):
+    """The layer's seven projections as plain linears, dense W against the rank-r factors (the
+    configured ranks, or every rank at `ratio` of min(dims)); `dense_us` reuses dense timings."""
     c = I.CFG2
     d, dff = c.d, c.d_ff
     shapes = {"q": (d, d), "k": (d, d), "v": (d, d), "o": (d, d), "gate": (d, dff), "up": (d, dff), "down": (dff, d)}
+    ranks = dict(c.ranks) if ratio is None else {p: I.rank_of(ratio, *shapes[p]) for p in shapes}
     gen = torch.Generator(device=dev)
     gen.manual_seed(7)
     bf = fsvd.FSVD_BF16
     res = {"config": f"dense_vs_lowrank_llama7b_m{M}", "rows": M, "projections": {}}
+    if ratio is not None:
+        res["rank_ratio"] = ratio
     tot_d = tot_l = by_d = by_l = fl_d = fl_l = 0.0
     for name, (K, N) in shapes.items():
-        r = c.ranks[name]
+        r = ranks[name]
         rs = (r + 31) // 32 * 32  # stored rank, as the layer stores it
         x = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -324,7 +330,8 @@ def run_dense_vs_lowrank(M, dev, stream, copies=4):
             Ut = torch.cat([Ut, torch.zeros((rs - r, K), dtype=Ut.dtype, device=dev)]) if rs > r else Ut
             Vt = pad_cols_dev(Vt, rs)
             fac.append((Ut, Vt))
-            dense.append((Vt.float() @ Ut.float()).to(torch.bfloat16))  # W [N, K] = (U V)^T
+            if dense_us is None:
+                dense.append((Vt.float() @ Ut.float()).to(torch.bfloat16))  # W [N, K] = (U V)^T
         ws = fsvd.workspace(fsvd.fsvd_lowrank_linear_ws(M, K, rs, N, bf), device=dev)
         it = {"d": 0, "l": 0}
 
@@ -339,7 +346,7 @@ def run_dense_vs_lowrank(M, dev, stream, copies=4):
             fsvd.fsvd_lowrank_linear(x, M, K, K, Ut, rs, K, Vt, N, rs, None, None, N, y, N, bf, ws, ws.numel(),
                                      stream)
 
-        t_d = timed_median(dense_call, stream, min_ms=10.0)
+        t_d = timed_median(dense_call, stream, min_ms=10.0) if dense_us is None else dense_us[name] * 1e-3
         t_l = timed_median(lowrank_call, stream, min_ms=10.0)
         b_d = 2 * (N * K + M * K + M * N)
         b_l = 2 * (r * (K + N) + M * K + M * N)
@@ -359,6 +366,20 @@ def run_dense_vs_lowrank(M, dev, stream, copies=4):
         res["dense_mfma_frac"] = round(fl_d / (tot_d * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
         res["lowrank_mfma_frac"] = round(fl_l / (tot_l * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
     return res
+
+
+def run_dense_vs_lowrank_ratios(M, dev, stream, ratios=(0.1, 0.2, 0.3, 0.4, 0.5, 0.6)):
+    """Low-rank speedup over the dense weights against the rank ratio (every projection at `ratio`
+    of min(dims)), the dense side timed once."""
+    base = run_dense_vs_lowrank(M, dev, stream)
+    dense_us = {p: v["dense_us"] for p, v in base["projections"].items()}
+    out = {"config": f"dense_vs_lowrank_ratios_llama7b_m{M}", "rows": M, "dense_us": base["dense_us"], "ratios": []}
+    for q in ratios:
+        r = run_dense_vs_lowrank(M, dev, stream, ratio=q, dense_us=dense_us)
+        out["ratios"].append({"rank_ratio": q, "lowrank_us": r["lowrank_us"], "lowrank_speedup": r["lowrank_speedup"],
+                              "byte_ratio": round(r["lowrank_bytes"] / r["dense_bytes"], 4),
+                              "flop_ratio": round(r["lowrank_flops"] / r["dense_flops"], 4)})
+    return out
 
 
 # ----------------------------------------------------------------------------- dense KV vs low-rank history
@@ -518,6 +539,8 @@ def main():
                                              stream)))
     for M in (1, 4, 8192):
         runs.append((f"dense_vs_lowrank_llama7b_m{M}", lambda M=M: run_dense_vs_lowrank(M, dev, stream)))
+    for M in (1, 4, 8192):
+        runs.append((f"dense_vs_lowrank_ratios_llama7b_m{M}", lambda M=M: run_dense_vs_lowrank_ratios(M, dev, stream)))
     for B in (1, 4):
         runs.append((f"attn_lowrank_history_llama7b_b{B}", lambda B=B: run_attn_history(B, 2048, dev, stream)))
     only = set(filter(None, args.only.split(",")))
