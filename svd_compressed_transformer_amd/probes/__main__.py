@@ -8,8 +8,9 @@ phase_boundary: a decode layer-step modelled as 10 dependent streaming phases, a
 graph against one persistent kernel with grid barriers, with and without prefetching the next
 phase's first loads before each barrier; then the 9 phases left with the attention merge inside
 the attention kernel, at the decode kernels' grids and at 512, 1024 and 2048 workgroups a phase,
-and with 25 / 50 / 100% of each next phase prefetched into the Infinity Cache (see
-phase_boundary.hip); one JSON line per variant.
+with 25 / 50 / 100% of each next phase prefetched into the Infinity Cache, and with each
+projection's two phases in one launch on separate workgroups (see phase_boundary.hip); one JSON
+line per variant.
 """
 from __future__ import annotations
 

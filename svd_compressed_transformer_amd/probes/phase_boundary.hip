@@ -24,6 +24,8 @@
 //             phases with every grid at 512, 1024 and 2048 workgroups.
 //   kernels9_mall: the 9 phases at the decode grids, each kernel reading 25 / 50 / 100% of the next
 //             phase's bytes with ordinary loads after its own stream (into the Infinity Cache).
+//   kernels9_pairs: the 9 phases with each projection's two phases in one launch on separate
+//             workgroups (pair_kernel), polling with s_sleep 1, 16 and 64 between reads.
 // A first argument n runs the variants from n on.
 //
 // Every activation word encodes (layer-step, phase, slot); each reader counts the words it does not
@@ -139,6 +141,86 @@ __global__ __launch_bounds__(256) void phase_mall_kernel(const u32x4* __restrict
         acc ^= a.x ^ a.y ^ a.z ^ a.w;
     }
     if (acc == 0x12345678u) sink[blockIdx.x & 63] = acc;  // keeps the loads live
+}
+
+// Two dependent phases in one launch, on separate workgroups: blocks [0, g1) do phase p (read the
+// activation the previous kernel wrote, stream their share of w1, write their activation slice with
+// agent-scope stores, wait for those stores, count themselves); blocks [g1, g1 + g2) first issue
+// every load of their share of w2 (at most PF 16-byte vectors per thread, the whole share at the
+// decode kernels' grids), then wait until all g1 blocks have counted, then read phase p's activation
+// with agent-scope loads and fold in the prefetched vectors; the last of them resets both counters.
+// Lower block indices are dispatched first, so the waiting blocks never hold back a phase-p block;
+// the wait is bounded (past spin_limit the error flag is set and the block exits).
+template <int SLEEP>
+__global__ __launch_bounds__(256) void pair_kernel(const u32x4* __restrict__ w1, long n1, const u32x4* __restrict__ w2,
+                                                   long n2, int g1, uint32_t* act, int p, int skip, uint32_t step,
+                                                   unsigned* cnt, unsigned* bad, unsigned* err, uint32_t* sink,
+                                                   unsigned spin_limit) {
+    uint32_t acc = 0;
+    const int g2 = gridDim.x - g1;
+    if ((int)blockIdx.x < g1) {
+        read_act<false>(act, step, p - skip, bad);
+        const long stride = (long)g1 * blockDim.x;
+        long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+        for (; i + 3 * stride < n1; i += 4 * stride) {
+            const u32x4 a = __builtin_nontemporal_load(w1 + i), b = __builtin_nontemporal_load(w1 + i + stride);
+            const u32x4 c = __builtin_nontemporal_load(w1 + i + 2 * stride), d = __builtin_nontemporal_load(w1 + i + 3 * stride);
+            acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+        }
+        for (; i < n1; i += stride) {
+            const u32x4 a = __builtin_nontemporal_load(w1 + i);
+            acc ^= a.x ^ a.y ^ a.z ^ a.w;
+        }
+        // this block's slice of the activation: blocks stride over the words as the phase kernels do
+        uint32_t* out = act + p * ACT;
+        for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < ACT / 4; j += g1 * blockDim.x) {
+            const u32x4 v = {act_word(step, p, 4 * j), act_word(step, p, 4 * j + 1), act_word(step, p, 4 * j + 2),
+                             act_word(step, p, 4 * j + 3)};
+            __builtin_amdgcn_raw_buffer_store_b128(v, rsrc(out), j * 16, 0, 16);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        const int b2 = blockIdx.x - g1;
+        const long stride = (long)g2 * blockDim.x;
+        const long t0 = (long)b2 * blockDim.x + threadIdx.x;
+        u32x4 pf[PF];
+#pragma unroll
+        for (int j = 0; j < PF; ++j) pf[j] = __builtin_nontemporal_load(w2 + std::min(t0 + j * stride, n2 - 1));
+        __shared__ int ok;
+        if (threadIdx.x == 0) {
+            unsigned it = 0;
+            ok = 1;
+            while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)g1) {
+                if (++it > spin_limit) { atomicOr(err, 1u); ok = 0; break; }
+                __builtin_amdgcn_s_sleep(SLEEP);
+            }
+        }
+        __syncthreads();
+        if (!ok) return;
+        read_act<true>(act, step, p + 1, bad);
+#pragma unroll
+        for (int j = 0; j < PF; ++j)
+            if (t0 + j * stride < n2) acc ^= pf[j].x ^ pf[j].y ^ pf[j].z ^ pf[j].w;
+        for (long i = t0 + (long)PF * stride; i < n2; i += stride) {
+            const u32x4 a = __builtin_nontemporal_load(w2 + i);
+            acc ^= a.x ^ a.y ^ a.z ^ a.w;
+        }
+        uint32_t* out = act + (p + 1) * ACT;
+        for (int j = b2 * blockDim.x + threadIdx.x; j < ACT / 4; j += g2 * blockDim.x)
+            reinterpret_cast<u32x4*>(out)[j] = u32x4{act_word(step, p + 1, 4 * j), act_word(step, p + 1, 4 * j + 1),
+                                                     act_word(step, p + 1, 4 * j + 2), act_word(step, p + 1, 4 * j + 3)};
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const unsigned old = __hip_atomic_fetch_add(cnt + 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (old + 1 == (unsigned)g2) {  // every block has passed its wait: reset for the next launch
+                __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(cnt + 32, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+    if (acc == 0x12345678u) sink[blockIdx.x & 63] = acc;
 }
 
 // two-level barrier number k (k = 1, 2, ...): XCD counter, the last arriver of an XCD bumps the
@@ -308,6 +390,8 @@ int main(int argc, char** argv) {
     uint32_t *act, *sink;
     unsigned *xcnt, *gcnt, *bad, *err;
     CK(hipMalloc(&act, (size_t)P * ACT * 4)); CK(hipMalloc(&sink, 64 * 4));
+    unsigned* pcnt;
+    CK(hipMalloc(&pcnt, 64 * 4));
     CK(hipMalloc(&xcnt, 8 * 32 * 4)); CK(hipMalloc(&gcnt, 4)); CK(hipMalloc(&bad, 4)); CK(hipMalloc(&err, 4));
     Phases ph[NL];
     for (int l = 0; l < NL; ++l) {
@@ -323,12 +407,13 @@ int main(int argc, char** argv) {
     // each copy's graph is captured with a fixed step and the activation check tolerates reuse by
     // writing before reading within the same graph (phase 0 reads nothing)
     CK(hipFuncSetAttribute((const void*)persist_lds_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, LDSV * 16));
-    constexpr int NV = 13;
+    constexpr int NV = 16;
     constexpr double MALL_F[3] = {0.25, 0.5, 1.0};  // variants 10-12: fraction of the next phase prefetched
     for (int variant = first; variant < NV; ++variant) {
         std::vector<float> v;
         for (int rep = 0; rep < 5; ++rep) {
             CK(hipMemsetAsync(xcnt, 0, 8 * 32 * 4, st)); CK(hipMemsetAsync(gcnt, 0, 4, st));
+            CK(hipMemsetAsync(pcnt, 0, 64 * 4, st));
             CK(hipMemsetAsync(bad, 0, 4, st)); CK(hipMemsetAsync(err, 0, 4, st));
             CK(hipStreamSynchronize(st));
             std::vector<hipGraphExec_t> ge;
@@ -343,6 +428,18 @@ int main(int argc, char** argv) {
                             continue;
                         }
                         if (GRID9[p] == 0) { skip = 1; continue; }
+                        if (variant >= 13) {  // phase pairs in one launch each; the attention alone
+                            if (p == 2) {
+                                phase_kernel<<<GRID9[p], 256, 0, st>>>(ph[l].w[p], n16[p], act, p, (uint32_t)l, bad, sink, 0);
+                            } else if (p % 2 == 0) {
+                                auto k = variant == 13 ? pair_kernel<1> : variant == 14 ? pair_kernel<16> : pair_kernel<64>;
+                                k<<<GRID9[p] + GRID9[p + 1], 256, 0, st>>>(
+                                    ph[l].w[p], n16[p], ph[l].w[p + 1], n16[p + 1], GRID9[p], act, p, skip, (uint32_t)l,
+                                    pcnt, bad, err, sink, 1u << 20);
+                            }
+                            skip = 0;
+                            continue;
+                        }
                         if (variant >= 10) {  // next phase: p + 1 (past the skipped merge), or the next copy's phase 0
                             int q = p + 1;
                             if (q < P && GRID9[q] == 0) ++q;
@@ -404,7 +501,8 @@ int main(int argc, char** argv) {
         const double us = v[2] * 1e3 / steps;
         const char* name[NV] = {"kernels", "persist", "prefetch", "persist_depth16", "prefetch_depth16", "lds_prefetch",
                                 "kernels9", "kernels9_grid512", "kernels9_grid1024", "kernels9_grid2048",
-                                "kernels9_mall25", "kernels9_mall50", "kernels9_mall100"};
+                                "kernels9_mall25", "kernels9_mall50", "kernels9_mall100", "kernels9_pairs",
+                                "kernels9_pairs_sleep16", "kernels9_pairs_sleep64"};
         const double vb = variant >= 6 ? bytes - (double)n16[3] * 16 : bytes;  // the 9 phases skip the merge's bytes
         printf("{\"variant\": \"%s\", \"us_per_layer_step\": %.2f, \"gbs\": %.1f, \"of_8tbs\": %.3f}\n", name[variant], us,
                vb / (us * 1e-6) / 1e9, vb / (us * 1e-6) / 8e12);
