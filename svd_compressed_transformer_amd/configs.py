@@ -33,6 +33,8 @@ One JSON line per measurement on stdout:
   8192 token rows, each once with the dense weight W = U.V (fsvd_dense_linear: one kernel) and once
   with the rank-1638 factors (fsvd_lowrank_linear: two kernels), through the same kernels; no
   norm, activation, RoPE or cache work on either side; 4 weight copies rotated.
+- gemm_vs_vendor_llama7b_shapes: the library's MFMA GEMM (y = x . W^T, 8192 rows) against the
+  vendor GEMM (hipBLASLt through torch.matmul, same bf16 operands) at the prefill products' (K, N).
 - dense_vs_lowrank_ratios_llama7b_m{1,4,8192}: the same at rank ratios 0.1-0.6 of min(dims) on every
   projection: the low-rank speedup over the dense weights against the compression ratio.
 - attn_lowrank_history_llama7b_b{1,4}: the decode attention of a Llama-7B-shaped layer over a
@@ -368,6 +370,38 @@ def run_dense_vs_lowrank(M, dev, stream, copies=4, ratio=None, dense_us=None):
     return res
 
 
+def run_gemm_vs_vendor(dev, stream, M=8192):
+    """The library's MFMA GEMM (fsvd_dense_linear: y = x . W^T) against the vendor GEMM (hipBLASLt,
+    through torch.matmul on the same bf16 operands) at the prefill products' shapes."""
+    bf = fsvd.FSVD_BF16
+    out = {"config": "gemm_vs_vendor_llama7b_shapes", "rows": M, "shapes": []}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3)
+    for K, N in ((4096, 4992), (1664, 4096), (4096, 1664), (4096, 3328), (11008, 1664), (1664, 12288),
+                 (4096, 4096)):
+        x = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16)
+        Ws = [torch.randn((N, K), generator=gen, device=dev).to(torch.bfloat16) for _ in range(2)]
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        it = [0]
+
+        def ours():
+            fsvd.fsvd_dense_linear(x, M, K, K, Ws[it[0] % 2], N, K, None, None, N, y, N, bf, stream)
+            it[0] += 1
+
+        def vendor():
+            torch.matmul(x, Ws[it[0] % 2].t(), out=y)
+            it[0] += 1
+
+        t_o = timed_median(ours, stream)
+        t_v = timed_median(vendor, stream)
+        fl = 2.0 * M * K * N
+        out["shapes"].append({"K": K, "N": N, "ours_us": round(t_o * 1e3, 1), "vendor_us": round(t_v * 1e3, 1),
+                              "ours_mfma_frac": round(fl / (t_o * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                              "vendor_mfma_frac": round(fl / (t_v * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)})
+        del x, Ws, y
+    return out
+
+
 def run_dense_vs_lowrank_ratios(M, dev, stream, ratios=(0.1, 0.2, 0.3, 0.4, 0.5, 0.6)):
     """Low-rank speedup over the dense weights against the rank ratio (every projection at `ratio`
     of min(dims)), the dense side timed once."""
@@ -539,6 +573,7 @@ def main():
                                              stream)))
     for M in (1, 4, 8192):
         runs.append((f"dense_vs_lowrank_llama7b_m{M}", lambda M=M: run_dense_vs_lowrank(M, dev, stream)))
+    runs.append(("gemm_vs_vendor_llama7b_shapes", lambda: run_gemm_vs_vendor(dev, stream)))
     for M in (1, 4, 8192):
         runs.append((f"dense_vs_lowrank_ratios_llama7b_m{M}", lambda M=M: run_dense_vs_lowrank_ratios(M, dev, stream)))
     for B in (1, 4):
