@@ -330,10 +330,19 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
             }
         }
     };
-    // passes of U steps, then single steps for the rest of the slice (no step past it is loaded)
+    // passes of U steps, then the rest of the slice in one pass, so all of its loads are in flight
+    // together (no step past the slice is loaded).  With 1-2 activation rows (U = 4) a wave's slice
+    // is usually 2 steps: one pass of 2, not two passes of 1 whose second waits for the first.
     int s0 = 0;
     for (; s0 + U <= nsteps; s0 += U) pass(std::integral_constant<int, U>(), s0);
-    for (; s0 < nsteps; ++s0) pass(std::integral_constant<int, 1>(), s0);
+    const int rest = nsteps - s0;  // 0 .. U - 1, wave-uniform
+    if constexpr (U >= 4) {
+        if (rest == 3) pass(std::integral_constant<int, 3>(), s0);
+        else if (rest == 2) pass(std::integral_constant<int, 2>(), s0);
+        else if (rest == 1) pass(std::integral_constant<int, 1>(), s0);
+    } else {
+        for (; s0 < nsteps; ++s0) pass(std::integral_constant<int, 1>(), s0);
+    }
 
     // Cross-lane reduction: a reduce-scatter over each 16-lane row leaves every lane with the row
     // sums of its own block of the wave's values (the kR x BMAX products and, in phase 1, the BMAX
