@@ -206,7 +206,10 @@ __device__ __forceinline__ void rowdot_epilogue(const RowdotArgs& a, const Rowdo
 }
 
 
-template <typename T, int BMAX, int EPI>
+// NW: phase 1 with an RMSNorm weight to apply to the activation (its loads and registers are left
+// out when the weight is folded into the factor or there is no norm: at 3-4 activation rows that
+// keeps the kernel at 96 registers, 5 waves per SIMD instead of 4)
+template <typename T, int BMAX, int EPI, bool NW = true>
 __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const RowdotArgs a) {
     constexpr int E = Vec<T>::E;
     // the wave index is uniform across the wave; saying so keeps every per-wave quantity (row
@@ -277,7 +280,7 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
     const int M = a.M;
     const int64_t lda_b = a.lda * (int64_t)sizeof(T);
     const bool norm = (EPI == EPI_Z) && a.norm;
-    const bool norm_w = norm && a.norm_w != nullptr;
+    const bool norm_w = NW && norm && a.norm_w != nullptr;
     // activation rows past M re-read row M - 1 (their results are never stored); without a norm
     // weight its loads read the activation instead (valid memory, value unused)
     const char* arow[BMAX];
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
             const int64_t kc = (int64_t)min(k, kc_max) * sizeof(T);
 #pragma unroll
             for (int r = 0; r < kR; ++r) wv[u][r] = ldg16_stream(wrow[r] + kc);
-            nw[u] = ldg16(nwp + kc);
+            if constexpr (EPI == EPI_Z && NW) nw[u] = ldg16(nwp + kc);
 #pragma unroll
             for (int b = 0; b < BMAX; ++b) av[u][b] = ldg16(arow[b] + kc);
         }
@@ -322,7 +325,9 @@ __global__ __launch_bounds__(BMAX >= 32 ? 256 : 512) void rowdot_kernel(const Ro
                 if constexpr (EPI == EPI_Z) {
                     if (norm) {
                         ss[b] = vsq(x, ss[b], T());
-                        if (norm_w) x = vmulw(x, nw[u]);
+                        if constexpr (NW) {
+                            if (norm_w) x = vmulw(x, nw[u]);
+                        }
                     }
                 }
 #pragma unroll
@@ -694,15 +699,25 @@ __global__ __launch_bounds__(512) void rowdot_mfma_kernel(const RowdotArgs a) {
                             64 * a.waves, val, ssq);
 }
 
+template <typename T, int EPI, bool NW>
+void launch_bm(const RowdotArgs& a, int grid, hipStream_t st) {
+    const int M = a.M;
+    if (M <= 1) rowdot_kernel<T, 1, EPI, NW><<<grid, 64 * a.waves, 0, st>>>(a);
+    else if (M <= 2) rowdot_kernel<T, 2, EPI, NW><<<grid, 64 * a.waves, 0, st>>>(a);
+    else if (M <= 4) rowdot_kernel<T, 4, EPI, NW><<<grid, 64 * a.waves, 0, st>>>(a);
+    else if (M <= 8) rowdot_kernel<T, 8, EPI, NW><<<grid, 64 * a.waves, 0, st>>>(a);
+    else if (M <= 16) rowdot_kernel<T, 16, EPI, NW><<<grid, 64 * a.waves, 0, st>>>(a);
+    else rowdot_kernel<T, 32, EPI, NW><<<grid, 64 * a.waves, 0, st>>>(a);
+}
+
 template <typename T, int EPI>
 fsvd_status_t launch_b(const RowdotArgs& a, int grid, hipStream_t st) {
-    const int M = a.M;
-    if (M <= 1) rowdot_kernel<T, 1, EPI><<<grid, 64 * a.waves, 0, st>>>(a);
-    else if (M <= 2) rowdot_kernel<T, 2, EPI><<<grid, 64 * a.waves, 0, st>>>(a);
-    else if (M <= 4) rowdot_kernel<T, 4, EPI><<<grid, 64 * a.waves, 0, st>>>(a);
-    else if (M <= 8) rowdot_kernel<T, 8, EPI><<<grid, 64 * a.waves, 0, st>>>(a);
-    else if (M <= 16) rowdot_kernel<T, 16, EPI><<<grid, 64 * a.waves, 0, st>>>(a);
-    else rowdot_kernel<T, 32, EPI><<<grid, 64 * a.waves, 0, st>>>(a);
+    if constexpr (EPI == EPI_Z) {
+        if (a.norm && a.norm_w != nullptr) launch_bm<T, EPI, true>(a, grid, st);
+        else launch_bm<T, EPI, false>(a, grid, st);
+    } else {
+        launch_bm<T, EPI, false>(a, grid, st);
+    }
     return check_launch("rowdot");
 }
 
